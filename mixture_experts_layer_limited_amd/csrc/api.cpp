@@ -1,0 +1,512 @@
+// C ABI of libmoe355 (include/moe355.h): argument validation, workspace
+// carving and the launch sequence of every entry point.  No allocation, no
+// host synchronisation: each call enqueues kernels on the caller's stream.
+#include "moe355.h"
+
+#include <math.h>
+#include <stddef.h>
+
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Sequential carving of the caller's workspace; with base == nullptr it only
+// measures.
+struct Carver {
+  char* base;
+  size_t used = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  template <class T>
+  T* take(size_t count) {
+    const size_t off = used;
+    used = align_up(used + count * sizeof(T));
+    return base ? (T*)(base + off) : nullptr;
+  }
+};
+
+bool is_fp8(const moe_config* c) { return c->weight_dtype == MOE_FP8_E4M3; }
+int act_dt(const moe_config* c) { return c->act_dtype == MOE_F32 ? MOE_DT_F32 : MOE_DT_BF16; }
+size_t act_bytes(const moe_config* c) { return c->act_dtype == MOE_F32 ? 4 : 2; }
+
+int check_cfg(const moe_config* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->scoring != MOE_SCORE_SOFTMAX && c->scoring != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (c->norm_topk_prob != 0 && c->norm_topk_prob != 1) return MOE_ERR_INVALID_ARG;
+  if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (c->weight_dtype != MOE_F32 && c->weight_dtype != MOE_BF16 && c->weight_dtype != MOE_FP8_E4M3)
+    return MOE_ERR_INVALID_ARG;
+  if (c->out_dtype != MOE_F32 && c->out_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (c->hidden <= 0 || c->inter <= 0 || c->n_experts <= 0 || c->top_k <= 0 || c->n_group <= 0 ||
+      c->topk_group <= 0 || c->shared_inter < 0)
+    return MOE_ERR_CONFIG;
+  if (!isfinite(c->routed_scaling_factor)) return MOE_ERR_CONFIG;
+  if (c->n_experts % c->n_group) return MOE_ERR_CONFIG;
+  if (c->topk_group > c->n_group) return MOE_ERR_CONFIG;
+  const int G = c->n_experts / c->n_group;
+  if (c->n_group > 1 && G < 2) return MOE_ERR_CONFIG;
+  if (c->top_k > c->n_experts) return MOE_ERR_CONFIG;
+  if (c->n_group > 1 && c->top_k > c->topk_group * G) return MOE_ERR_CONFIG;
+  // Limits of this implementation.
+  if (c->n_experts > 1024 || c->top_k > 32 || c->n_group > 64) return MOE_ERR_UNSUPPORTED;
+  if (c->out_dtype != c->act_dtype) return MOE_ERR_UNSUPPORTED;
+  if (c->weight_dtype != c->act_dtype && !(c->weight_dtype == MOE_FP8_E4M3 && c->act_dtype == MOE_BF16))
+    return MOE_ERR_UNSUPPORTED;
+  const int mult = is_fp8(c) ? 128 : 64;
+  if (c->hidden % mult || c->inter % mult || c->shared_inter % mult) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_T(const moe_config* c, int64_t T) {
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T * (int64_t)c->top_k >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  if (T * (int64_t)c->n_experts >= (int64_t)1 << 40) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  (void)hipGetLastError();
+  return MOE_ERR_HIP;
+}
+
+#define MOE_TRY(expr)                 \
+  do {                                \
+    const int _st = (expr);           \
+    if (_st != MOE_OK) return _st;    \
+  } while (0)
+#define HIP_TRY(expr) MOE_TRY(hip_status(expr))
+
+int max_mtiles(int64_t rows, int bm, int groups) {
+  if (rows <= 0) return 0;
+  const int64_t bound = rows / bm + groups;
+  return (int)(bound < rows ? bound : rows);
+}
+
+// ------------------------------------------------------------- workspace ---
+
+struct RouteWs { float* logits; };
+void carve_route(Carver& cv, const moe_config* c, int64_t T, RouteWs& w) {
+  w.logits = cv.take<float>((size_t)T * c->n_experts);
+}
+
+struct PermuteWs { int32_t* counts; };
+void carve_permute(Carver& cv, const moe_config* c, int64_t T, PermuteWs& w) {
+  const int nb = permute_blocks((int)(T * c->top_k));
+  w.counts = cv.take<int32_t>((size_t)nb * c->n_experts);
+}
+
+// Workspace of one grouped SwiGLU over `rows` permuted rows of `groups` experts
+// with intermediate size I.
+struct SwigluWs {
+  int4* tiles1; int* ntiles1;
+  int4* tiles2; int* ntiles2;
+  void* h;                    // intermediate, act dtype (bf16 for FP8 weights)
+  uint8_t* hq; float* h_scales; // FP8: E4M3 intermediate + 1x128 scales
+  uint8_t* xq; float* xs;
+  float* row_w;
+};
+void carve_swiglu(Carver& cv, const moe_config* c, int64_t T, int64_t rows, int groups, int I,
+                  bool quantize_x, bool scatter, SwigluWs& w) {
+  const int64_t avg = rows / groups;
+  const GemmShape g1 = is_fp8(c) ? gemm_fp8_shape((int)avg) : gemm_shape(0, (int)avg, groups);
+  const GemmShape g2 = is_fp8(c) ? gemm_fp8_shape((int)avg) : gemm_shape(1, (int)avg, groups);
+  w.tiles1 = cv.take<int4>((size_t)max_mtiles(rows, g1.bm, groups) + 1);
+  w.ntiles1 = cv.take<int>(1);
+  w.tiles2 = cv.take<int4>((size_t)max_mtiles(rows, g2.bm, groups) + 1);
+  w.ntiles2 = cv.take<int>(1);
+  if (is_fp8(c)) {
+    w.h = cv.take<uint16_t>((size_t)rows * I);
+    w.hq = cv.take<uint8_t>((size_t)rows * I);
+    w.h_scales = cv.take<float>((size_t)rows * (I / 128));
+    if (quantize_x) {
+      w.xq = cv.take<uint8_t>((size_t)T * c->hidden);
+      w.xs = cv.take<float>((size_t)T * (c->hidden / 128));
+    } else {
+      w.xq = nullptr; w.xs = nullptr;
+    }
+  } else {
+    w.h = cv.take<char>((size_t)rows * I * act_bytes(c));
+    w.hq = nullptr; w.h_scales = nullptr; w.xq = nullptr; w.xs = nullptr;
+  }
+  w.row_w = scatter ? cv.take<float>((size_t)rows) : nullptr;
+}
+
+struct ForwardWs {
+  RouteWs route;
+  PermuteWs perm;
+  SwigluWs routed, shared;
+  float* scores; int32_t* ids; float* topw;
+  int32_t* offsets; int32_t* src; int32_t* inv;
+  void* y; float* acc;
+  void* sh_out;
+};
+void carve_forward(Carver& cv, const moe_config* c, int64_t T, bool scatter, ForwardWs& w) {
+  const int64_t rows = T * c->top_k;
+  w.scores = cv.take<float>((size_t)T * c->n_experts);
+  w.ids = cv.take<int32_t>((size_t)rows);
+  w.topw = cv.take<float>((size_t)rows);
+  w.offsets = cv.take<int32_t>((size_t)c->n_experts + 1);
+  w.src = cv.take<int32_t>((size_t)rows);
+  w.inv = cv.take<int32_t>((size_t)rows);
+  carve_permute(cv, c, T, w.perm);
+  carve_swiglu(cv, c, T, rows, c->n_experts, c->inter, true, scatter, w.routed);
+  if (scatter) {
+    w.y = nullptr;
+    w.acc = cv.take<float>((size_t)T * c->hidden);
+  } else {
+    w.y = cv.take<char>((size_t)rows * c->hidden * act_bytes(c));
+    w.acc = nullptr;
+  }
+  if (c->shared_inter > 0) {
+    carve_swiglu(cv, c, T, T, 1, c->shared_inter, false, false, w.shared);
+    w.sh_out = cv.take<char>((size_t)T * c->hidden * act_bytes(c));
+  } else {
+    w.sh_out = nullptr;
+  }
+}
+
+// ------------------------------------------------------------ sequences ---
+
+int do_route(const moe_config* c, int64_t T, const void* hidden, const void* gate_w, const float* bias,
+             const float* scores_in, float* scores_out, int32_t* ids, float* topw, float* logits_ws,
+             hipStream_t s) {
+  RouteParams rp{};
+  rp.bias = bias;
+  rp.topk_ids = ids;
+  rp.topk_w = topw;
+  rp.T = (int)T; rp.E = c->n_experts; rp.k = c->top_k;
+  rp.n_group = c->n_group; rp.topk_group = c->topk_group;
+  rp.scoring = c->scoring; rp.norm = c->norm_topk_prob; rp.scale = c->routed_scaling_factor;
+  if (scores_in) {
+    rp.logits = scores_in;
+    rp.scores_given = 1;
+    rp.scores_out = nullptr;
+  } else {
+    // Logits land where the scores go (in place per element), else in the workspace.
+    float* logits = scores_out ? scores_out : logits_ws;
+    GemmParams g{};
+    g.A = hidden; g.a_rows = nullptr;
+    g.B = gate_w; g.b_gstride = 0;
+    g.K = c->hidden; g.N = c->n_experts;
+    g.C = logits;
+    g.tiles = nullptr;
+    const GemmShape sh = gemm_shape(2, (int)T, 1);
+    g.M = (int)T;
+    g.n_mtiles = (int)((T + sh.bm - 1) / sh.bm);
+    g.ntn = (c->n_experts + sh.bn - 1) / sh.bn;
+    HIP_TRY(launch_gemm(act_dt(c), EPI_STORE, MOE_DT_F32, g, sh, g.n_mtiles, s));
+    rp.logits = logits;
+    rp.scores_given = 0;
+    rp.scores_out = scores_out;
+  }
+  HIP_TRY(launch_route(rp, s));
+  return MOE_OK;
+}
+
+// m-tiles from the device list, or dense rows [0, rows) when there are no offsets.
+template <class P>
+void set_tiles(P& p, bool dense, int64_t rows, int bm, const int4* tiles, const int* ntiles) {
+  if (dense) {
+    p.tiles = nullptr; p.n_mtiles_dev = nullptr;
+    p.M = (int)rows; p.n_mtiles = (int)((rows + bm - 1) / bm);
+  } else {
+    p.tiles = tiles; p.n_mtiles_dev = ntiles;
+  }
+}
+
+// One grouped SwiGLU: routed experts (offsets given) or a dense FFN over all
+// rows (offsets == nullptr, the shared expert).
+int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, const void* hidden,
+              const float* hidden_scales, const int32_t* src, const int32_t* offsets, const void* w13,
+              const float* w13_s, const void* w2, const float* w2_s, int epi, const float* topk_w,
+              const int32_t* inv, void* out, float* acc, const SwigluWs& w, hipStream_t s,
+              hipEvent_t const* ev = nullptr) {
+  auto mark = [&](int i) -> int {
+    if (ev && ev[i]) return hip_status(hipEventRecord(ev[i], s));
+    return MOE_OK;
+  };
+  const int H = c->hidden;
+  const int64_t avg = rows / groups;
+  if (is_fp8(c)) {
+    const uint8_t* xq = (const uint8_t*)hidden;
+    const float* xs = hidden_scales;
+    if (!hidden_scales) {  // quantise the activations first
+      HIP_TRY(launch_quantize(act_dt(c), T, H, hidden, w.xq, w.xs, s));
+      xq = w.xq; xs = w.xs;
+    }
+    const GemmShape g = gemm_fp8_shape((int)avg);
+    const bool dense = offsets == nullptr;
+    if (!dense) HIP_TRY(launch_build_mtiles(offsets, groups, g.bm, w.tiles1, w.ntiles1, s));
+    GemmFp8Params p{};
+    p.A = xq; p.a_scales = xs; p.a_rows = src;
+    p.B = (const uint8_t*)w13; p.b_scales = w13_s;
+    p.b_gstride = (int64_t)2 * I * H; p.bs_gstride = (int64_t)(2 * I / 128) * (H / 128);
+    p.K = H; p.N = I;
+    p.C = w.h;
+    set_tiles(p, dense, rows, g.bm, w.tiles1, w.ntiles1);
+    p.ntn = (I + g.bn / 2 - 1) / (g.bn / 2);
+    const int gm = dense ? p.n_mtiles : max_mtiles(rows, g.bm, groups);
+    MOE_TRY(mark(0));
+    HIP_TRY(launch_gemm_fp8(EPI_SWIGLU, p, g, gm, s));
+    MOE_TRY(mark(1));
+    HIP_TRY(launch_quantize(MOE_DT_BF16, rows, I, w.h, w.hq, w.h_scales, s));
+    GemmFp8Params q{};
+    q.A = w.hq; q.a_scales = w.h_scales; q.a_rows = nullptr;
+    q.B = (const uint8_t*)w2; q.b_scales = w2_s;
+    q.b_gstride = (int64_t)H * I; q.bs_gstride = (int64_t)(H / 128) * (I / 128);
+    q.K = I; q.N = H;
+    set_tiles(q, dense, rows, g.bm, w.tiles1, w.ntiles1);
+    q.ntn = (H + g.bn - 1) / g.bn;
+    if (epi == MOE_EPI_SCATTER_ADD) {
+      HIP_TRY(launch_row_weights(topk_w, inv, (int)rows, w.row_w, s));
+      q.C = acc; q.c_rows = src; q.row_w = w.row_w;
+      MOE_TRY(mark(2));
+      HIP_TRY(launch_gemm_fp8(EPI_SCATTER, q, g, gm, s));
+    } else {
+      q.C = out;
+      MOE_TRY(mark(2));
+      HIP_TRY(launch_gemm_fp8(EPI_STORE, q, g, gm, s));
+    }
+    return mark(3);
+  }
+  const int dt = act_dt(c);
+  const GemmShape g1 = gemm_shape(0, (int)avg, groups);
+  const GemmShape g2 = gemm_shape(1, (int)avg, groups);
+  const bool dense = offsets == nullptr;
+  if (!dense) HIP_TRY(launch_build_mtiles(offsets, groups, g1.bm, w.tiles1, w.ntiles1, s));
+  GemmParams p{};
+  p.A = hidden; p.a_rows = src;
+  p.B = w13; p.b_gstride = (int64_t)2 * I * H;
+  p.K = H; p.N = I; p.C = w.h;
+  set_tiles(p, dense, rows, g1.bm, w.tiles1, w.ntiles1);
+  p.ntn = (I + g1.bn / 2 - 1) / (g1.bn / 2);
+  MOE_TRY(mark(0));
+  HIP_TRY(launch_gemm(dt, EPI_SWIGLU, dt, p, g1, dense ? p.n_mtiles : max_mtiles(rows, g1.bm, groups), s));
+  MOE_TRY(mark(1));
+
+  const int4* t2 = w.tiles1;
+  const int* n2 = w.ntiles1;
+  if (!dense && g2.bm != g1.bm) {
+    HIP_TRY(launch_build_mtiles(offsets, groups, g2.bm, w.tiles2, w.ntiles2, s));
+    t2 = w.tiles2; n2 = w.ntiles2;
+  }
+  GemmParams q{};
+  q.A = w.h; q.a_rows = nullptr;
+  q.B = w2; q.b_gstride = (int64_t)H * I;
+  q.K = I; q.N = H;
+  set_tiles(q, dense, rows, g2.bm, t2, n2);
+  q.ntn = (H + g2.bn - 1) / g2.bn;
+  const int gm2 = dense ? q.n_mtiles : max_mtiles(rows, g2.bm, groups);
+  if (epi == MOE_EPI_SCATTER_ADD) {
+    HIP_TRY(launch_row_weights(topk_w, inv, (int)rows, w.row_w, s));
+    q.C = acc; q.c_rows = src; q.row_w = w.row_w;
+    MOE_TRY(mark(2));
+    HIP_TRY(launch_gemm(dt, EPI_SCATTER, MOE_DT_F32, q, g2, gm2, s));
+  } else {
+    q.C = out;
+    MOE_TRY(mark(2));
+    HIP_TRY(launch_gemm(dt, EPI_STORE, dt, q, g2, gm2, s));
+  }
+  return mark(3);
+}
+
+}  // namespace
+
+// ================================================================== ABI ===
+
+extern "C" {
+
+int moe_version(void) { return MOE355_VERSION; }
+
+const char* moe_strerror(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_CONFIG: return "inconsistent layer configuration";
+    case MOE_ERR_UNSUPPORTED: return "configuration not supported by this library";
+    case MOE_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case MOE_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_validate_config(const moe_config* cfg) { return check_cfg(cfg); }
+
+size_t moe_workspace_size(const moe_config* c, int64_t T, int32_t op) {
+  if (check_cfg(c) != MOE_OK || T < 0 || check_T(c, T) != MOE_OK) return 0;
+  if (T == 0) return 0;
+  Carver cv(nullptr);
+  switch (op) {
+    case MOE_OP_ROUTE: { RouteWs w; carve_route(cv, c, T, w); break; }
+    case MOE_OP_PERMUTE: { PermuteWs w; carve_permute(cv, c, T, w); break; }
+    case MOE_OP_GROUPED_SWIGLU: {
+      // Sized for the routed experts and for a one-group shared call of the same T.
+      SwigluWs w;
+      Carver a(nullptr), b(nullptr);
+      carve_swiglu(a, c, T, T * c->top_k, c->n_experts, c->inter, true, true, w);
+      if (c->shared_inter > 0) carve_swiglu(b, c, T, T, 1, c->shared_inter, true, true, w);
+      return a.used > b.used ? a.used : b.used;
+    }
+    case MOE_OP_COMBINE: return 0;
+    case MOE_OP_FORWARD: {
+      ForwardWs a, b;
+      Carver ca(nullptr), cb(nullptr);
+      carve_forward(ca, c, T, false, a);
+      carve_forward(cb, c, T, true, b);
+      return ca.used > cb.used ? ca.used : cb.used;
+    }
+    default: return 0;
+  }
+  return cv.used;
+}
+
+static int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return MOE_OK;
+  if (!ws || ((uintptr_t)ws % kAlign) || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+int moe_route(const moe_config* c, int64_t T, const void* hidden, const void* gate_w, const float* bias,
+              const float* scores_in, float* scores_out, int32_t* topk_ids, float* topk_w, void* ws,
+              size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_cfg(c));
+  MOE_TRY(check_T(c, T));
+  if (!topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!scores_in && (!hidden || !gate_w)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  RouteWs w{};
+  if (!scores_in && !scores_out) {
+    Carver probe(nullptr);
+    carve_route(probe, c, T, w);
+    MOE_TRY(check_ws(ws, ws_bytes, probe.used));
+    Carver cv(ws);
+    carve_route(cv, c, T, w);
+  }
+  return do_route(c, T, hidden, gate_w, bias, scores_in, scores_out, topk_ids, topk_w, w.logits, stream);
+}
+
+int moe_permute(const moe_config* c, int64_t T, const int32_t* topk_ids, int32_t* expert_offsets,
+                int32_t* permuted_src, int32_t* inv_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_cfg(c));
+  MOE_TRY(check_T(c, T));
+  if (!topk_ids || !expert_offsets || !permuted_src || !inv_perm) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  Carver probe(nullptr);
+  PermuteWs w;
+  carve_permute(probe, c, T, w);
+  MOE_TRY(check_ws(ws, ws_bytes, probe.used));
+  Carver cv(ws);
+  carve_permute(cv, c, T, w);
+  HIP_TRY(launch_permute(topk_ids, (int)(T * c->top_k), c->top_k, c->n_experts, w.counts, expert_offsets,
+                         permuted_src, inv_perm, stream));
+  return MOE_OK;
+}
+
+int moe_grouped_swiglu(const moe_config* c, int64_t T, const void* hidden, const float* hidden_scales,
+                       const int32_t* permuted_src, const int32_t* expert_offsets, const void* w13,
+                       const float* w13_scales, const void* w2, const float* w2_scales, int32_t epilogue,
+                       const float* topk_w, const int32_t* inv_perm, void* expert_out, float* acc, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_cfg(c));
+  MOE_TRY(check_T(c, T));
+  if (epilogue != MOE_EPI_STORE_ROWS && epilogue != MOE_EPI_SCATTER_ADD) return MOE_ERR_INVALID_ARG;
+  if (!hidden || !expert_offsets || !w13 || !w2) return MOE_ERR_INVALID_ARG;
+  if (is_fp8(c) && (!w13_scales || !w2_scales)) return MOE_ERR_INVALID_ARG;
+  if (hidden_scales && !is_fp8(c)) return MOE_ERR_INVALID_ARG;
+  if (epilogue == MOE_EPI_STORE_ROWS && !expert_out) return MOE_ERR_INVALID_ARG;
+  if (epilogue == MOE_EPI_SCATTER_ADD && (!acc || !topk_w || !inv_perm)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  const int64_t rows = T * c->top_k;
+  const bool scatter = epilogue == MOE_EPI_SCATTER_ADD;
+  Carver probe(nullptr);
+  SwigluWs w;
+  carve_swiglu(probe, c, T, rows, c->n_experts, c->inter, hidden_scales == nullptr, scatter, w);
+  MOE_TRY(check_ws(ws, ws_bytes, probe.used));
+  Carver cv(ws);
+  carve_swiglu(cv, c, T, rows, c->n_experts, c->inter, hidden_scales == nullptr, scatter, w);
+  return do_swiglu(c, T, rows, c->n_experts, c->inter, hidden, hidden_scales, permuted_src, expert_offsets, w13,
+                   w13_scales, w2, w2_scales, epilogue, topk_w, inv_perm, expert_out, acc, w, stream);
+}
+
+int moe_combine(const moe_config* c, int64_t T, const void* expert_out, const float* acc, const int32_t* inv_perm,
+                const float* topk_w, const void* shared_out, void* out, hipStream_t stream) {
+  MOE_TRY(check_cfg(c));
+  MOE_TRY(check_T(c, T));
+  if (!out) return MOE_ERR_INVALID_ARG;
+  if (expert_out && (!inv_perm || !topk_w)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  HIP_TRY(launch_combine(act_dt(c), (int)T, c->hidden, c->top_k, expert_out, acc, inv_perm, topk_w, shared_out,
+                         out, stream));
+  return MOE_OK;
+}
+
+int moe_forward(const moe_config* c, int64_t T, const void* hidden, const void* gate_w, const float* bias,
+                const void* w13, const float* w13_scales, const void* w2, const float* w2_scales,
+                const void* sh_w13, const float* sh_w13_scales, const void* sh_w2, const float* sh_w2_scales,
+                void* out, const moe_forward_opts* opts, void* ws, size_t ws_bytes, hipStream_t stream) {
+  MOE_TRY(check_cfg(c));
+  MOE_TRY(check_T(c, T));
+  if (!hidden || !gate_w || !w13 || !w2 || !out) return MOE_ERR_INVALID_ARG;
+  if (is_fp8(c) && (!w13_scales || !w2_scales)) return MOE_ERR_INVALID_ARG;
+  if (c->shared_inter > 0 && (!sh_w13 || !sh_w2)) return MOE_ERR_INVALID_ARG;
+  if (c->shared_inter > 0 && is_fp8(c) && (!sh_w13_scales || !sh_w2_scales)) return MOE_ERR_INVALID_ARG;
+  const int epi = opts ? opts->epilogue : MOE_EPI_STORE_ROWS;
+  if (epi != MOE_EPI_STORE_ROWS && epi != MOE_EPI_SCATTER_ADD) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  const bool scatter = epi == MOE_EPI_SCATTER_ADD;
+  Carver probe(nullptr);
+  ForwardWs w;
+  carve_forward(probe, c, T, scatter, w);
+  MOE_TRY(check_ws(ws, ws_bytes, probe.used));
+  Carver cv(ws);
+  carve_forward(cv, c, T, scatter, w);
+
+  float* scores = (opts && opts->scores) ? opts->scores : w.scores;
+  int32_t* ids = (opts && opts->topk_ids) ? opts->topk_ids : w.ids;
+  float* topw = (opts && opts->topk_w) ? opts->topk_w : w.topw;
+  int32_t* offsets = (opts && opts->expert_offsets) ? opts->expert_offsets : w.offsets;
+  int32_t* src = (opts && opts->permuted_src) ? opts->permuted_src : w.src;
+  int32_t* inv = (opts && opts->inv_perm) ? opts->inv_perm : w.inv;
+  const int64_t rows = T * c->top_k;
+
+  MOE_TRY(do_route(c, T, hidden, gate_w, bias, nullptr, scores, ids, topw, nullptr, stream));
+  HIP_TRY(launch_permute(ids, (int)rows, c->top_k, c->n_experts, w.perm.counts, offsets, src, inv, stream));
+
+  // Shared expert first: its quantised activations (FP8) are reused by the routed experts.
+  const float* xs = nullptr;
+  const void* xin = hidden;
+  if (is_fp8(c)) {
+    HIP_TRY(launch_quantize(act_dt(c), T, c->hidden, hidden, w.routed.xq, w.routed.xs, stream));
+    xin = w.routed.xq;
+    xs = w.routed.xs;
+  }
+  if (c->shared_inter > 0) {
+    moe_config sc = *c;
+    sc.n_experts = 1; sc.top_k = 1; sc.inter = c->shared_inter; sc.n_group = 1; sc.topk_group = 1;
+    MOE_TRY(do_swiglu(&sc, T, T, 1, c->shared_inter, xin, xs, nullptr, nullptr, sh_w13, sh_w13_scales, sh_w2,
+                      sh_w2_scales, MOE_EPI_STORE_ROWS, nullptr, nullptr, w.sh_out, nullptr, w.shared, stream));
+  }
+  if (scatter) HIP_TRY(launch_fill_zero(w.acc, T * c->hidden, stream));
+  MOE_TRY(do_swiglu(c, T, rows, c->n_experts, c->inter, xin, xs, src, offsets, w13, w13_scales, w2, w2_scales, epi,
+                    topw, inv, w.y, w.acc, w.routed, stream, opts ? opts->events : nullptr));
+  HIP_TRY(launch_combine(act_dt(c), (int)T, c->hidden, c->top_k, w.y, w.acc, inv, topw, w.sh_out, out, stream));
+  return MOE_OK;
+}
+
+int moe_quantize_fp8_1x128(int64_t rows, int64_t cols, const void* in, int32_t in_dtype, uint8_t* codes,
+                           float* scales, hipStream_t stream) {
+  if (rows < 0 || cols < 0 || (cols % 128)) return MOE_ERR_INVALID_ARG;
+  if (in_dtype != MOE_F32 && in_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (rows == 0 || cols == 0) return MOE_OK;
+  if (!in || !codes || !scales) return MOE_ERR_INVALID_ARG;
+  HIP_TRY(launch_quantize(in_dtype == MOE_F32 ? MOE_DT_F32 : MOE_DT_BF16, rows, cols, in, codes, scales, stream));
+  return MOE_OK;
+}
+
+}  // extern "C"

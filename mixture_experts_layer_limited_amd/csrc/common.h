@@ -1,0 +1,131 @@
+// Device-side helpers shared by the gfx950 kernels of libmoe355.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------ bf16 ---
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Element storage traits: F32 = float, BF16 = uint16_t bits.
+template <int DT> struct Elem;
+template <> struct Elem<0> {  // MOE_F32
+  using T = float;
+  static constexpr int kBytes = 4;
+  __device__ static float load(const T* p, int64_t i) { return p[i]; }
+  __device__ static void store(T* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<1> {  // MOE_BF16
+  using T = uint16_t;
+  static constexpr int kBytes = 2;
+  __device__ static float load(const T* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
+  __device__ static void store(T* p, int64_t i, float v) { p[i] = (uint16_t)f32_to_bf16_bits(v); }
+};
+
+// ------------------------------------------------------- wave reductions ---
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    uint32_t w = (uint32_t)__shfl_xor((int)v, o, 64);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// Order-preserving map of a non-NaN float to uint32 (a < b  <=>  key(a) < key(b)).
+// -0.0 and +0.0 must be canonicalised by the caller (add 0.0f) to compare equal.
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------- E4M3FN ---
+
+// Round-to-nearest-even fp32 -> OCP E4M3FN with saturation to +-448; sign kept
+// (so tiny negatives give -0), NaN -> 0x7F.  Written from the format: 1 sign,
+// 4 exponent bits with bias 7, 3 mantissa bits, subnormals at exponent field 0.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;
+  float m = __uint_as_float(a);
+  if (m >= 448.0f) return sign | 0x7eu;
+  uint32_t code;
+  if (m < 0.015625f) {                       // below 2^-6: subnormal step 2^-9
+    // m * 2^9 rounded to nearest even integer, 0..8 (8 = smallest normal)
+    float q = m * 512.0f;                    // exact (power-of-two scaling)
+    uint32_t qi = (uint32_t)q;               // floor
+    float r = q - (float)qi;                 // exact
+    if (r > 0.5f || (r == 0.5f && (qi & 1u))) qi += 1;
+    code = qi;                               // 8 encodes 2^-6 = exponent field 1, mantissa 0
+  } else {
+    // normal: keep 3 mantissa bits of the fp32 value with RNE on the 20 dropped bits
+    uint32_t e = (a >> 23) - 127 + 7;        // biased E4M3 exponent, 1..15
+    uint32_t mant = a & 0x7fffffu;
+    uint32_t keep = mant >> 20;
+    uint32_t rest = mant & 0xfffffu;
+    uint32_t half = 0x80000u;
+    if (rest > half || (rest == half && (keep & 1u))) keep += 1;
+    code = (e << 3) + keep;                  // mantissa carry bumps the exponent
+    if (code > 0x7eu) code = 0x7eu;          // rounding up past 448 saturates
+  }
+  return sign | code;
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  uint32_t s = c & 0x80u, e = (c >> 3) & 0xfu, m = c & 7u;
+  float v = (e == 0) ? (float)m * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return s ? -v : v;
+}
+
+// ----------------------------------------------------- workgroup mapping ---
+
+// Work-groups are handed to the 8 XCDs round-robin by id.  Remap a physical id
+// P in [0, n) to a logical id so that consecutive logical ids land on the same
+// XCD (and share its L2).
+__device__ __forceinline__ int xcd_remap(int P, int n) {
+  constexpr int kXcd = 8;
+  int q = n / kXcd, r = n % kXcd;
+  int x = P % kXcd, local = P / kXcd;
+  return x * q + (x < r ? x : r) + local;
+}
+
+}  // namespace moe

@@ -1,0 +1,269 @@
+// Grouped FP8 E4M3 GEMMs with fine-grained fp32 scales (MoA routing + FP8
+// inference, blog.hotdry.top, FP8 section: E4M3, 1x128 activation tiles and
+// 128x128 weight blocks; V3 lab page, gsyq.cn/news/313569, §3 infer.toml
+// weight_block_size [128, 128]).
+//
+// C[p, n] = sum_kb sa[src(p), kb] * sb[n/128, kb] * sum_{k in kb} qa[src(p), k] * qb[n, k]
+//
+// One K step is exactly one 128-wide scale block: the two 32x32x64 MFMAs of a
+// step accumulate the unscaled partial product in fp32 and the partial is then
+// folded into the accumulator with the product of the row's activation scale
+// (staged in LDS) and the tile's weight-block scale.  Operand staging, the
+// m-tile list and the work-group mapping are those of the bf16 kernel.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+__device__ __forceinline__ f32x16 mma_fp8(const u32x4& a0, const u32x4& a1, const u32x4& b0, const u32x4& b1,
+                                          f32x16 c) {
+  const i32x8 a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  const i32x8 b = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+  // formats 0/0 = E4M3 for both operands; E8M0 scale 127 = 1.0 (the fp32 block
+  // scales are applied outside the MFMA)
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ float silu_mul8(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+template <int WM, int WN, int TM, int TN, int EPI>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_kernel(GemmFp8Params p) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int BM = WM * TM * 32;
+  constexpr int BN = WN * TN * 32;
+  constexpr int CA = BM * 8 / NT;
+  constexpr int CB = BN * 8 / NT;
+  static_assert(CA * NT == BM * 8 && CB * NT == BN * 8, "tile / thread mismatch");
+  static_assert(EPI != EPI_SWIGLU || TN % 2 == 0, "SwiGLU pairs gate and up tiles");
+  static_assert(BM <= NT, "one activation scale per thread");
+  constexpr int STAGE = (BM + BN) * 8;                 // u32x4 per operand stage
+  extern __shared__ u32x4 lds[];
+  float* sa_lds = (float*)(lds + 2 * STAGE);           // [2][BM]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  const int total_m = p.tiles ? *p.n_mtiles_dev : p.n_mtiles;
+  const int total = total_m * p.ntn;
+  const int P = blockIdx.x;
+  if (P >= total) return;
+  const int L = xcd_remap(P, total);
+  const int mt = L / p.ntn, nt = L - mt * p.ntn;
+  int grp, r0, r1;
+  if (p.tiles) {
+    const int4 t = p.tiles[mt];
+    grp = t.x; r0 = t.y; r1 = t.z;
+  } else {
+    grp = 0; r0 = mt * BM; r1 = min(p.M, r0 + BM);
+  }
+  const int rows = r1 - r0;
+  const int64_t K = p.K;
+  const int nkb = p.K / 128;
+  const uint8_t* Bg = p.B + (int64_t)grp * p.b_gstride;
+  const float* SBg = p.b_scales + (int64_t)grp * p.bs_gstride;
+
+  const uint8_t* aptr[CA];
+  bool aok[CA];
+  int aoff[CA];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) {
+    const int q = tid + i * NT, r = q >> 3, c = q & 7;
+    aok[i] = r < rows;
+    int src = 0;
+    if (aok[i]) src = p.a_rows ? p.a_rows[r0 + r] : r0 + r;
+    aptr[i] = p.A + (int64_t)src * K + c * 16;
+    aoff[i] = r * 8 + (c ^ (r & 7));
+  }
+  // activation-scale row of thread tid (tid < BM)
+  const bool sok = tid < rows;
+  const float* sap = p.a_scales;
+  if (sok) sap += (int64_t)(p.a_rows ? p.a_rows[r0 + tid] : r0 + tid) * nkb;
+
+  const uint8_t* bptr[CB];
+  int boff[CB];
+#pragma unroll
+  for (int i = 0; i < CB; ++i) {
+    const int q = tid + i * NT, r = q >> 3, c = q & 7;
+    int wrow;
+    if constexpr (EPI == EPI_SWIGLU) {
+      int j = min(nt * (BN / 2) + (r % (BN / 2)), p.N - 1);
+      wrow = (r < BN / 2) ? j : p.N + j;
+    } else {
+      wrow = min(nt * BN + r, p.N - 1);
+    }
+    bptr[i] = Bg + (int64_t)wrow * K + c * 16;
+    boff[i] = (BM + r) * 8 + (c ^ (r & 7));
+  }
+
+  auto bblock = [&](int tn) {
+    if constexpr (EPI == EPI_SWIGLU)
+      return tn < TN / 2 ? wn * (TN / 2) + tn : WN * (TN / 2) + wn * (TN / 2) + (tn - TN / 2);
+    else
+      return wn * TN + tn;
+  };
+  // weight-block row (of 128) of every wave tile column
+  int sbrow[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int bb = bblock(j) * 32;
+    int wrow;
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int j0 = min(nt * (BN / 2) + (bb % (BN / 2)), p.N - 1);
+      wrow = (bb < BN / 2) ? j0 : p.N + j0;
+    } else {
+      wrow = min(nt * BN + bb, p.N - 1);
+    }
+    sbrow[j] = wrow / 128;
+  }
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  int tm_live = 0;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+    if ((wm * TM + i) * 32 < rows) tm_live = i + 1;
+
+  u32x4 ra[CA], rb[CB];
+  float rsa = 0.0f;
+#define MOE_GLOAD(kt_)                                                       \
+  do {                                                                       \
+    const int64_t ko_ = (int64_t)(kt_) * 128;                                \
+    _Pragma("unroll") for (int i = 0; i < CA; ++i) if (aok[i]) ra[i] =       \
+        *(const u32x4*)(aptr[i] + ko_);                                      \
+    _Pragma("unroll") for (int i = 0; i < CB; ++i) rb[i] =                   \
+        *(const u32x4*)(bptr[i] + ko_);                                      \
+    if (sok) rsa = sap[kt_];                                                 \
+  } while (0)
+#define MOE_SSTORE(buf_)                                                     \
+  do {                                                                       \
+    u32x4* s_ = lds + (buf_) * STAGE;                                        \
+    _Pragma("unroll") for (int i = 0; i < CA; ++i) if (aok[i]) s_[aoff[i]] = ra[i]; \
+    _Pragma("unroll") for (int i = 0; i < CB; ++i) s_[boff[i]] = rb[i];      \
+    if (tid < BM) sa_lds[(buf_) * BM + tid] = sok ? rsa : 0.0f;              \
+  } while (0)
+
+  MOE_GLOAD(0);
+  MOE_SSTORE(0);
+  __syncthreads();
+
+  const int sw = lane & 7, lr = lane & 31, hi = lane >> 5;
+  for (int kt = 0; kt < nkb; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nkb) MOE_GLOAD(kt + 1);
+    if (tm_live > 0) {
+      const u32x4* s = lds + buf * STAGE;
+      float sb[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sb[j] = SBg[(int64_t)sbrow[j] * nkb + kt];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        if (i >= tm_live) continue;
+        const int arow = (wm * TM + i) * 32 + lr;
+        // lanes 0-31 take chunks {0,1} then {4,5}; lanes 32-63 take {2,3} then {6,7}
+        const u32x4 a00 = s[arow * 8 + ((4 * 0 + 2 * hi + 0) ^ sw)];
+        const u32x4 a01 = s[arow * 8 + ((4 * 0 + 2 * hi + 1) ^ sw)];
+        const u32x4 a10 = s[arow * 8 + ((4 * 1 + 2 * hi + 0) ^ sw)];
+        const u32x4 a11 = s[arow * 8 + ((4 * 1 + 2 * hi + 1) ^ sw)];
+        float sa[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          sa[e] = sa_lds[buf * BM + (wm * TM + i) * 32 + 8 * (e >> 2) + 4 * hi + (e & 3)];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int brow = BM + bblock(j) * 32 + lr;
+          const u32x4 b00 = s[brow * 8 + ((2 * hi + 0) ^ sw)];
+          const u32x4 b01 = s[brow * 8 + ((2 * hi + 1) ^ sw)];
+          const u32x4 b10 = s[brow * 8 + ((4 + 2 * hi + 0) ^ sw)];
+          const u32x4 b11 = s[brow * 8 + ((4 + 2 * hi + 1) ^ sw)];
+          f32x16 part;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) part[e] = 0.0f;
+          part = mma_fp8(a00, a01, b00, b01, part);
+          part = mma_fp8(a10, a11, b10, b11, part);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[i][j][e] += part[e] * (sa[e] * sb[j]);
+        }
+      }
+    }
+    if (kt + 1 < nkb) MOE_SSTORE(buf ^ 1);
+    __syncthreads();
+  }
+#undef MOE_GLOAD
+#undef MOE_SSTORE
+
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    if (i >= tm_live) continue;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = (wm * TM + i) * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+      if (row >= rows) continue;
+      const int prow = r0 + row;
+      if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int j = 0; j < TN / 2; ++j) {
+          const int col = nt * (BN / 2) + (wn * (TN / 2) + j) * 32 + lr;
+          if (col < p.N)
+            ((uint16_t*)p.C)[(int64_t)prow * p.N + col] =
+                (uint16_t)f32_to_bf16_bits(silu_mul8(acc[i][j][e], acc[i][j + TN / 2][e]));
+        }
+      } else if constexpr (EPI == EPI_SCATTER) {
+        const int tok = p.c_rows ? p.c_rows[prow] : prow;
+        const float w = p.row_w[prow];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = nt * BN + bblock(j) * 32 + lr;
+          if (col < p.N) atomicAdd((float*)p.C + (int64_t)tok * p.N + col, w * acc[i][j][e]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = nt * BN + bblock(j) * 32 + lr;
+          if (col < p.N) ((uint16_t*)p.C)[(int64_t)prow * p.N + col] = (uint16_t)f32_to_bf16_bits(acc[i][j][e]);
+        }
+      }
+    }
+  }
+}
+
+GemmShape gemm_fp8_shape(int rows_hint) {
+  GemmShape g;
+  (void)rows_hint;
+  g.bm = 128; g.bn = 128; g.kind = 0;
+  return g;
+}
+
+template <int WM, int WN, int TM, int TN, int EPI>
+static hipError_t launch8(const GemmFp8Params& p, int grid_m, hipStream_t s) {
+  constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+  constexpr int lds_bytes = 2 * (BM + BN) * 128 + 2 * BM * 4;
+  auto kern = gemm_fp8_kernel<WM, WN, TM, TN, EPI>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t grid = (int64_t)grid_m * p.ntn;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WM * WN * 64), lds_bytes, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp8(int epi, const GemmFp8Params& p, const GemmShape& g, int grid_m, hipStream_t s) {
+  (void)g;
+  switch (epi) {
+    case EPI_SWIGLU: return launch8<2, 2, 2, 2, EPI_SWIGLU>(p, grid_m, s);
+    case EPI_SCATTER: return launch8<2, 2, 2, 2, EPI_SCATTER>(p, grid_m, s);
+    case EPI_STORE: return launch8<2, 2, 2, 2, EPI_STORE>(p, grid_m, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace moe

@@ -1,0 +1,90 @@
+// Internal launch interface between the C-ABI layer (api.cpp) and the
+// kernels (*.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1, MOE_DT_FP8 = 2 };
+enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SCATTER = 2 };
+
+struct GemmParams {
+  const void* A;          // activations: row src(p) at A + src(p) * K elements
+  const int32_t* a_rows;  // src(p) = a_rows[p]; NULL: src(p) = p
+  const void* B;          // weights of group g at B + g * b_gstride elements, (out, in)
+  int64_t b_gstride;
+  int K;                  // reduction length (elements)
+  int N;                  // output columns; SwiGLU: h columns (B holds 2N rows)
+  void* C;                // output: rows p (store, SwiGLU) or rows c_rows[p] (scatter)
+  const int32_t* c_rows;  // scatter: output row of row p; NULL: p
+  const float* row_w;     // scatter: weight of row p
+  const int4* tiles;      // m-tiles {group, row0, row1, -}; NULL: dense rows [0, M)
+  const int* n_mtiles_dev;
+  int n_mtiles;           // dense: number of m-tiles
+  int M;                  // dense: rows
+  int ntn;                // number of n-tiles
+};
+
+struct GemmShape {
+  int bm = 128;
+  int bn = 128;  // weight rows per tile (SwiGLU: bn/2 h columns)
+  int kind = 0;
+};
+
+GemmShape gemm_shape(int kind, int rows_hint, int n_groups);
+hipError_t launch_gemm(int dt, int epi, int odt, const GemmParams& p, const GemmShape& g, int grid_m,
+                       hipStream_t s);
+hipError_t launch_build_mtiles(const int32_t* offsets, int E, int bm, int4* tiles, int* n_tiles,
+                               hipStream_t s);
+
+// FP8 grouped GEMM: A = E4M3 codes with 1x128 fp32 scales, B = E4M3 codes with
+// 128x128 fp32 block scales.
+struct GemmFp8Params {
+  const uint8_t* A;
+  const float* a_scales;  // [rowsA, K/128]
+  const int32_t* a_rows;
+  const uint8_t* B;
+  const float* b_scales;  // group g: b_scales + g * bs_gstride, [Nrows/128, K/128]
+  int64_t b_gstride;      // bytes between groups
+  int64_t bs_gstride;     // floats between groups
+  int K;
+  int N;
+  void* C;                // SwiGLU: bf16 h [rows, N]; store: bf16 [rows, N]; scatter: fp32 [T, N]
+  const int32_t* c_rows;
+  const float* row_w;
+  const int4* tiles;
+  const int* n_mtiles_dev;
+  int n_mtiles;
+  int M;
+  int ntn;
+};
+GemmShape gemm_fp8_shape(int rows_hint);
+hipError_t launch_gemm_fp8(int epi, const GemmFp8Params& p, const GemmShape& g, int grid_m, hipStream_t s);
+
+struct RouteParams {
+  const float* logits;    // [T,E] router logits, or scores when scores_given
+  int scores_given;
+  const float* bias;      // [E] or NULL
+  float* scores_out;      // [T,E] or NULL
+  int32_t* topk_ids;
+  float* topk_w;
+  int T, E, k, n_group, topk_group, scoring, norm;
+  float scale;
+};
+hipError_t launch_route(const RouteParams& p, hipStream_t s);
+
+hipError_t launch_permute(const int32_t* ids, int n, int k, int E, int32_t* counts, int32_t* offsets,
+                          int32_t* src, int32_t* inv, hipStream_t s);
+int permute_blocks(int n);
+
+hipError_t launch_row_weights(const float* topk_w, const int32_t* inv, int n, float* row_w, hipStream_t s);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+hipError_t launch_combine(int adt, int T, int H, int k, const void* expert_out, const float* acc,
+                          const int32_t* inv, const float* topk_w, const void* shared_out, void* out,
+                          hipStream_t s);
+hipError_t launch_quantize(int in_dt, int64_t rows, int64_t cols, const void* in, uint8_t* codes,
+                           float* scales, hipStream_t s);
+
+}  // namespace moe

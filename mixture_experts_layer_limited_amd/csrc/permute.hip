@@ -1,0 +1,114 @@
+// Token permutation (MoE inference walkthrough, zhiyuanblog.org/blog/moe-inference,
+// §3.2): a stable counting sort of the T*k copies by expert.
+//
+//   1. perm_hist:    per chunk of kChunk copies, an LDS histogram over experts
+//   2. perm_scan:    one block turns the (chunk, expert) counts into each
+//                    chunk's first slot per expert, and expert_offsets
+//   3. perm_scatter: one wavefront per chunk walks its copies in order, 64 at a
+//                    time; lanes with equal experts are found with ballots over
+//                    the expert id bits, ranked by lane, and placed after the
+//                    running count of their expert, so the order is stable and
+//                    the result is the same on every run (no atomics decide
+//                    a position).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kChunk = 1024;
+
+int permute_blocks(int n) { return (n + kChunk - 1) / kChunk; }
+
+__global__ __launch_bounds__(256) void perm_hist(const int32_t* __restrict__ ids, int n, int E,
+                                                 int32_t* __restrict__ counts) {
+  __shared__ int h[1024];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) h[e] = 0;
+  __syncthreads();
+  const int base = blockIdx.x * kChunk;
+  for (int i = threadIdx.x; i < kChunk; i += blockDim.x) {
+    const int a = base + i;
+    if (a < n) {
+      const int e = min(max(ids[a], 0), E - 1);
+      atomicAdd(&h[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) counts[(int64_t)blockIdx.x * E + e] = h[e];
+}
+
+// One block of 1024 threads, thread e owns expert e (E <= 1024).  Rewrites
+// counts[b][e] in place into the first permuted slot of chunk b for expert e.
+__global__ __launch_bounds__(1024) void perm_scan(int32_t* __restrict__ counts, int nb, int E,
+                                                  int32_t* __restrict__ offsets) {
+  __shared__ int scan[1024];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E)
+    for (int b = 0; b < nb; ++b) total += counts[(int64_t)b * E + e];
+  scan[e] = total;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = e >= o ? scan[e - o] : 0;
+    __syncthreads();
+    scan[e] += v;
+    __syncthreads();
+  }
+  const int excl = scan[e] - total;
+  if (e < E) {
+    offsets[e] = excl;
+    int run = excl;
+    for (int b = 0; b < nb; ++b) {
+      const int c = counts[(int64_t)b * E + e];
+      counts[(int64_t)b * E + e] = run;
+      run += c;
+    }
+  }
+  if (e == E - 1) offsets[E] = excl + total;
+}
+
+__global__ __launch_bounds__(64) void perm_scatter(const int32_t* __restrict__ ids, int n, int k, int E,
+                                                   const int32_t* __restrict__ first,
+                                                   int32_t* __restrict__ src, int32_t* __restrict__ inv) {
+  __shared__ int run[1024];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) run[e] = first[(int64_t)blockIdx.x * E + e];
+  __syncthreads();
+  int bits = 0;
+  while ((1 << bits) < E) ++bits;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int base = blockIdx.x * kChunk;
+  for (int g = 0; g < kChunk; g += 64) {
+    const int a = base + g + lane;
+    const bool ok = a < n;
+    const int e = ok ? min(max(ids[a], 0), E - 1) : 0;
+    uint64_t same = __ballot(ok);
+    for (int b = 0; b < bits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      same &= bit ? bal : ~bal;
+    }
+    const int rank = __popcll(same & lt);
+    const int pos = run[e] + rank;
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): every lane has read run[] before it changes
+    __builtin_amdgcn_wave_barrier();
+    if (ok && rank == 0) run[e] = pos + __popcll(same);
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+    if (ok) {
+      src[pos] = a / k;
+      inv[a] = pos;
+    }
+  }
+}
+
+hipError_t launch_permute(const int32_t* ids, int n, int k, int E, int32_t* counts, int32_t* offsets,
+                          int32_t* src, int32_t* inv, hipStream_t s) {
+  const int nb = permute_blocks(n);
+  if (nb == 0) return hipSuccess;
+  hipLaunchKernelGGL(perm_hist, dim3(nb), dim3(256), 0, s, ids, n, E, counts);
+  hipLaunchKernelGGL(perm_scan, dim3(1), dim3(1024), 0, s, counts, nb, E, offsets);
+  hipLaunchKernelGGL(perm_scatter, dim3(nb), dim3(64), 0, s, ids, n, k, E, counts, src, inv);
+  return hipGetLastError();
+}
+
+}  // namespace moe

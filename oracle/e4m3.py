@@ -21,9 +21,9 @@ import numpy as np
 E4M3_MAX = 448.0
 
 
-def e4m3_decode(codes: np.ndarray) -> np.ndarray:
-    """Exact fp64 value of every E4M3FN code (NaN for the two NaN codes)."""
-    c = np.asarray(codes, np.uint8).astype(np.int64)
+def _decode_from_fields(c: np.ndarray) -> np.ndarray:
+    """Value of codes c from the bit fields of the format."""
+    c = np.asarray(c).astype(np.int64)
     sign = np.where(c & 0x80, -1.0, 1.0)
     exp = (c >> 3) & 0xF
     man = c & 0x7
@@ -32,6 +32,15 @@ def e4m3_decode(codes: np.ndarray) -> np.ndarray:
     mag = np.where(exp == 0, subnormal, normal)
     mag = np.where((exp == 15) & (man == 7), np.nan, mag)
     return sign * mag
+
+
+_TABLE = _decode_from_fields(np.arange(256))                 # all 256 codes, fp64
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Exact fp64 value of every E4M3FN code (NaN for the two NaN codes),
+    looked up in the table of all 256 codes built from the bit fields."""
+    return _TABLE[np.asarray(codes, np.uint8)]
 
 
 _POS_CODES = np.arange(0, 0x7F, dtype=np.uint8)          # 0 .. 126: all finite non-negatives

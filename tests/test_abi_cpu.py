@@ -1,0 +1,138 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point include/moe355.h declares, and rejects invalid arguments
+with the documented status before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_limited_amd as moe
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe355.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("moe_route", "moe_permute", "moe_grouped_swiglu", "moe_combine", "moe_forward",
+              "moe_workspace_size", "moe_strerror"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert set(declared_functions()) == set(moe.EXPORTS)
+    assert L.moe_version() == 1
+
+
+V3 = dict(hidden=7168, inter=2048, n_experts=256, top_k=8, n_group=8, topk_group=4, shared_inter=2048,
+          scoring="sigmoid", norm_topk_prob=True, routed_scaling_factor=2.5)
+
+
+def cfg(**kw):
+    d = dict(V3)
+    d.update(kw)
+    return moe.make_config(**d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, 0),
+    (dict(dtype="fp8"), 0),
+    (dict(dtype="f32"), 0),
+    (dict(n_group=7), -2),                    # E % n_group
+    (dict(topk_group=9), -2),                 # topk_group > n_group
+    (dict(top_k=129, topk_group=4), -2),      # k > topk_group * G
+    (dict(top_k=300), -2),                    # k > E
+    (dict(n_experts=256, n_group=256, topk_group=1, top_k=1), -2),   # groups of one expert
+    (dict(hidden=0), -2),
+    (dict(routed_scaling_factor=float("inf")), -2),
+    (dict(hidden=7168 + 32), -3),             # not a multiple of 64
+    (dict(dtype="fp8", inter=2048 + 64), -3), # FP8 needs multiples of 128
+    (dict(n_experts=2048, n_group=8), -3),    # E > 1024
+    (dict(top_k=33, topk_group=8), -3),       # k > 32
+])
+def test_config_validation(kw, status):
+    assert moe.validate_config(cfg(**kw)) == status
+
+
+def test_bad_enums_are_invalid_args():
+    c = cfg()
+    c.scoring = 7
+    assert moe.validate_config(c) == -1
+    c = cfg()
+    c.act_dtype = 2                             # activations cannot be FP8
+    assert moe.validate_config(c) == -1
+    c = cfg()
+    c.out_dtype = 0                             # output dtype must equal the activation dtype
+    assert moe.validate_config(c) == -3
+
+
+def test_workspace_sizes():
+    c = cfg()
+    assert moe.workspace_size(c, 0) == 0
+    sizes = [moe.workspace_size(c, T) for T in (1, 128, 8192)]
+    assert sizes[0] > 0 and sizes[0] < sizes[1] < sizes[2]
+    # the forward workspace holds the intermediate h (T*k*I bf16) and the expert rows (T*k*H bf16)
+    T = 8192
+    assert sizes[2] >= T * 8 * 2048 * 2 + T * 8 * 7168 * 2
+    assert moe.workspace_size(c, T, moe.MOE_OP_COMBINE) == 0
+    assert moe.workspace_size(c, T, moe.MOE_OP_ROUTE) >= T * 256 * 4
+    bad = cfg(n_group=7)
+    assert moe.workspace_size(bad, 128) == 0
+
+
+def _call(fn, *args):
+    return fn(*args)
+
+
+def test_entry_points_reject_before_launch():
+    """Invalid arguments come back as status codes; nothing is launched (this
+    runs without a GPU, where any launch would fail differently)."""
+    L = moe.lib()
+    c = cfg()
+    bad = cfg(n_group=7)
+    p = ctypes.c_void_p(0x1000)         # never dereferenced: validation fails first
+    null = None
+    b = ctypes.byref
+    assert L.moe_route(b(bad), 16, p, p, null, null, null, p, p, p, 1 << 30, null) == -2
+    assert L.moe_route(b(c), -1, p, p, null, null, null, p, p, p, 1 << 30, null) == -1
+    assert L.moe_route(b(c), 16, p, p, null, null, null, null, p, p, 1 << 30, null) == -1   # no topk_ids
+    assert L.moe_route(b(c), 16, null, p, null, null, null, p, p, p, 1 << 30, null) == -1   # no hidden
+    assert L.moe_route(b(c), 16, p, p, null, null, null, p, p, null, 0, null) == -4         # no workspace
+    assert L.moe_route(b(c), 16, p, p, null, null, null, p, p, ctypes.c_void_p(0x1001), 1 << 30, null) == -4
+    assert L.moe_route(b(c), 16, p, p, null, null, null, p, p, p, 16, null) == -4           # too small
+    assert L.moe_route(b(c), 0, p, p, null, null, null, p, p, null, 0, null) == 0           # T = 0: no-op
+    assert L.moe_permute(b(c), 16, null, p, p, p, p, 1 << 30, null) == -1
+    assert L.moe_permute(b(c), 16, p, p, p, p, p, 4, null) == -4
+    assert L.moe_grouped_swiglu(b(c), 16, p, null, p, p, p, null, p, null, 5, null, null, p, null, p, 1 << 30,
+                                null) == -1      # bad epilogue
+    assert L.moe_grouped_swiglu(b(c), 16, p, null, p, p, p, null, p, null, 1, null, null, null, p, p, 1 << 30,
+                                null) == -1      # scatter without weights
+    fp8 = cfg(dtype="fp8")
+    assert L.moe_grouped_swiglu(b(fp8), 16, p, null, p, p, p, null, p, null, 0, null, null, p, null, p,
+                                1 << 30, null) == -1      # FP8 without scales
+    assert L.moe_combine(b(c), 16, p, null, null, p, null, p, null) == -1   # rows without inv_perm
+    assert L.moe_combine(b(c), 16, null, null, null, null, null, null, null) == -1
+    assert L.moe_forward(b(c), 16, p, p, null, p, null, p, null, null, null, null, null, p, null, p, 1 << 40,
+                         null) == -1      # shared expert configured, no shared weights
+    opts = moe.ForwardOpts(9, None, None, None, None, None, None)
+    assert L.moe_forward(b(c), 16, p, p, null, p, null, p, null, p, null, p, null, p, b(opts), p, 1 << 40,
+                         null) == -1      # bad epilogue
+    assert L.moe_forward(b(c), 16, p, p, null, p, null, p, null, p, null, p, null, p, null, p, 8, null) == -4
+    assert L.moe_quantize_fp8_1x128(4, 100, p, 1, p, p, null) == -1
+    assert L.moe_quantize_fp8_1x128(4, 128, p, 2, p, p, null) == -1
+
+
+def test_strerror():
+    L = moe.lib()
+    for s in (0, -1, -2, -3, -4, -5):
+        assert L.moe_strerror(s).decode() not in ("", "unknown status")
+    assert L.moe_strerror(42).decode() == "unknown status"
