@@ -16,7 +16,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe355.so")
+# MOE355_LIB names another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("MOE355_LIB", os.path.join(_HERE, "libmoe355.so"))
 
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1

@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libmoe355.so")
 ARCH = "gfx950"
 
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC",
     # no packed fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",

@@ -82,6 +82,8 @@ int hip_status(hipError_t e) {
   } while (0)
 #define HIP_TRY(expr) MOE_TRY(hip_status(expr))
 
+int ntiles_n(int n, int bn) { return (n + bn - 1) / bn; }
+
 int max_mtiles(int64_t rows, int bm, int groups) {
   if (rows <= 0) return 0;
   const int64_t bound = rows / bm + groups;
@@ -101,6 +103,16 @@ void carve_permute(Carver& cv, const moe_config* c, int64_t T, PermuteWs& w) {
   w.counts = cv.take<int32_t>((size_t)nb * c->n_experts);
 }
 
+// Tile shapes of the gate/up and down GEMMs of one grouped SwiGLU.
+GemmShape shape1(const moe_config* c, int64_t T, int64_t rows, int groups, int I) {
+  const int64_t eb = act_bytes(c);
+  return gemm_shape(0, act_dt(c), (int)(rows / groups), T * c->hidden * eb, (int64_t)2 * I * c->hidden * eb);
+}
+GemmShape shape2(const moe_config* c, int64_t rows, int groups, int I) {
+  const int64_t eb = act_bytes(c);
+  return gemm_shape(1, act_dt(c), (int)(rows / groups), rows * I * eb, (int64_t)c->hidden * I * eb);
+}
+
 // Workspace of one grouped SwiGLU over `rows` permuted rows of `groups` experts
 // with intermediate size I.
 struct SwigluWs {
@@ -114,11 +126,12 @@ struct SwigluWs {
 void carve_swiglu(Carver& cv, const moe_config* c, int64_t T, int64_t rows, int groups, int I,
                   bool quantize_x, bool scatter, SwigluWs& w) {
   const int64_t avg = rows / groups;
-  const GemmShape g1 = is_fp8(c) ? gemm_fp8_shape((int)avg) : gemm_shape(0, (int)avg, groups);
-  const GemmShape g2 = is_fp8(c) ? gemm_fp8_shape((int)avg) : gemm_shape(1, (int)avg, groups);
-  w.tiles1 = cv.take<int4>((size_t)max_mtiles(rows, g1.bm, groups) + 1);
+  const GemmShape g1 = is_fp8(c) ? gemm_fp8_shape((int)avg) : shape1(c, T, rows, groups, I);
+  const GemmShape g2 = is_fp8(c) ? gemm_fp8_shape((int)avg) : shape2(c, rows, groups, I);
+  // tile lists: every (m-tile, n-tile) pair of the gate/up and of the down GEMM
+  w.tiles1 = cv.take<int4>((size_t)max_mtiles(rows, g1.bm, groups) * ntiles_n(I, g1.bn / 2) + 1);
   w.ntiles1 = cv.take<int>(1);
-  w.tiles2 = cv.take<int4>((size_t)max_mtiles(rows, g2.bm, groups) + 1);
+  w.tiles2 = cv.take<int4>((size_t)max_mtiles(rows, g2.bm, groups) * ntiles_n(c->hidden, g2.bn) + 1);
   w.ntiles2 = cv.take<int>(1);
   if (is_fp8(c)) {
     w.h = cv.take<uint16_t>((size_t)rows * I);
@@ -196,8 +209,9 @@ int do_route(const moe_config* c, int64_t T, const void* hidden, const void* gat
     g.K = c->hidden; g.N = c->n_experts;
     g.C = logits;
     g.tiles = nullptr;
-    const GemmShape sh = gemm_shape(2, (int)T, 1);
+    const GemmShape sh = gemm_shape(2, act_dt(c), (int)T, 0, 0);
     g.M = (int)T;
+    g.a_nrows = T;
     g.n_mtiles = (int)((T + sh.bm - 1) / sh.bm);
     g.ntn = (c->n_experts + sh.bn - 1) / sh.bn;
     HIP_TRY(launch_gemm(act_dt(c), EPI_STORE, MOE_DT_F32, g, sh, g.n_mtiles, s));
@@ -242,7 +256,11 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
     }
     const GemmShape g = gemm_fp8_shape((int)avg);
     const bool dense = offsets == nullptr;
-    if (!dense) HIP_TRY(launch_build_mtiles(offsets, groups, g.bm, w.tiles1, w.ntiles1, s));
+    const int ntn1 = ntiles_n(I, g.bn / 2), ntn2 = ntiles_n(H, g.bn);
+    if (!dense) {
+      HIP_TRY(launch_build_tiles(offsets, groups, g.bm, ntn1, w.tiles1, w.ntiles1, s));
+      HIP_TRY(launch_build_tiles(offsets, groups, g.bm, ntn2, w.tiles2, w.ntiles2, s));
+    }
     GemmFp8Params p{};
     p.A = xq; p.a_scales = xs; p.a_rows = src;
     p.B = (const uint8_t*)w13; p.b_scales = w13_s;
@@ -250,7 +268,7 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
     p.K = H; p.N = I;
     p.C = w.h;
     set_tiles(p, dense, rows, g.bm, w.tiles1, w.ntiles1);
-    p.ntn = (I + g.bn / 2 - 1) / (g.bn / 2);
+    p.ntn = ntn1;
     const int gm = dense ? p.n_mtiles : max_mtiles(rows, g.bm, groups);
     MOE_TRY(mark(0));
     HIP_TRY(launch_gemm_fp8(EPI_SWIGLU, p, g, gm, s));
@@ -261,8 +279,8 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
     q.B = (const uint8_t*)w2; q.b_scales = w2_s;
     q.b_gstride = (int64_t)H * I; q.bs_gstride = (int64_t)(H / 128) * (I / 128);
     q.K = I; q.N = H;
-    set_tiles(q, dense, rows, g.bm, w.tiles1, w.ntiles1);
-    q.ntn = (H + g.bn - 1) / g.bn;
+    set_tiles(q, dense, rows, g.bm, w.tiles2, w.ntiles2);
+    q.ntn = ntn2;
     if (epi == MOE_EPI_SCATTER_ADD) {
       HIP_TRY(launch_row_weights(topk_w, inv, (int)rows, w.row_w, s));
       q.C = acc; q.c_rows = src; q.row_w = w.row_w;
@@ -276,32 +294,32 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
     return mark(3);
   }
   const int dt = act_dt(c);
-  const GemmShape g1 = gemm_shape(0, (int)avg, groups);
-  const GemmShape g2 = gemm_shape(1, (int)avg, groups);
+  const GemmShape g1 = shape1(c, T, rows, groups, I);
+  const GemmShape g2 = shape2(c, rows, groups, I);
   const bool dense = offsets == nullptr;
-  if (!dense) HIP_TRY(launch_build_mtiles(offsets, groups, g1.bm, w.tiles1, w.ntiles1, s));
+  const int ntn1 = ntiles_n(I, g1.bn / 2), ntn2 = ntiles_n(H, g2.bn);
+  if (!dense) {
+    HIP_TRY(launch_build_tiles(offsets, groups, g1.bm, ntn1, w.tiles1, w.ntiles1, s));
+    HIP_TRY(launch_build_tiles(offsets, groups, g2.bm, ntn2, w.tiles2, w.ntiles2, s));
+  }
   GemmParams p{};
   p.A = hidden; p.a_rows = src;
   p.B = w13; p.b_gstride = (int64_t)2 * I * H;
   p.K = H; p.N = I; p.C = w.h;
+  p.a_nrows = T;
   set_tiles(p, dense, rows, g1.bm, w.tiles1, w.ntiles1);
-  p.ntn = (I + g1.bn / 2 - 1) / (g1.bn / 2);
+  p.ntn = ntn1;
   MOE_TRY(mark(0));
   HIP_TRY(launch_gemm(dt, EPI_SWIGLU, dt, p, g1, dense ? p.n_mtiles : max_mtiles(rows, g1.bm, groups), s));
   MOE_TRY(mark(1));
 
-  const int4* t2 = w.tiles1;
-  const int* n2 = w.ntiles1;
-  if (!dense && g2.bm != g1.bm) {
-    HIP_TRY(launch_build_mtiles(offsets, groups, g2.bm, w.tiles2, w.ntiles2, s));
-    t2 = w.tiles2; n2 = w.ntiles2;
-  }
   GemmParams q{};
   q.A = w.h; q.a_rows = nullptr;
   q.B = w2; q.b_gstride = (int64_t)H * I;
   q.K = I; q.N = H;
-  set_tiles(q, dense, rows, g2.bm, t2, n2);
-  q.ntn = (H + g2.bn - 1) / g2.bn;
+  q.a_nrows = rows;
+  set_tiles(q, dense, rows, g2.bm, w.tiles2, w.ntiles2);
+  q.ntn = ntn2;
   const int gm2 = dense ? q.n_mtiles : max_mtiles(rows, g2.bm, groups);
   if (epi == MOE_EPI_SCATTER_ADD) {
     HIP_TRY(launch_row_weights(topk_w, inv, (int)rows, w.row_w, s));

@@ -58,17 +58,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
-  const int total_m = p.tiles ? *p.n_mtiles_dev : p.n_mtiles;
-  const int total = total_m * p.ntn;
+  // device list: every (m-tile, n-tile) pair; dense: n_mtiles x ntn tiles
+  const int total = p.tiles ? *p.n_mtiles_dev : p.n_mtiles * p.ntn;
   const int P = blockIdx.x;
   if (P >= total) return;
   const int L = xcd_remap(P, total);
-  const int mt = L / p.ntn, nt = L - mt * p.ntn;
-  int grp, r0, r1;
+  int grp, r0, r1, nt;
   if (p.tiles) {
-    const int4 t = p.tiles[mt];
-    grp = t.x; r0 = t.y; r1 = t.z;
+    const int4 t = p.tiles[L];
+    grp = t.x; r0 = t.y; r1 = t.z; nt = t.w;
   } else {
+    const int mt = L / p.ntn;
+    nt = L - mt * p.ntn;
     grp = 0; r0 = mt * BM; r1 = min(p.M, r0 + BM);
   }
   const int rows = r1 - r0;
@@ -220,10 +221,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
 
 // ------------------------------------------------------------ m-tile list ---
 
-// One block: m-tiles of at most `bm` rows for every expert, in expert order.
-__global__ __launch_bounds__(1024) void build_mtiles_kernel(const int32_t* __restrict__ offsets, int E,
-                                                             int bm, int4* __restrict__ tiles,
-                                                             int* __restrict__ n_tiles) {
+// One block: the tile list of a grouped GEMM.  Expert e's rows are split into
+// c_e = ceil(rows / bm) m-tiles of near-equal size; the list holds every
+// (m-tile, n-tile) pair, expert by expert, n-tile by n-tile, with the c_e
+// m-tiles of one n-tile next to each other.  Neighbouring entries run at the
+// same time on the same XCD (see xcd_remap), so the m-tiles that share a
+// weight tile read it from that XCD's L2 instead of from HBM.
+// Entry: {expert, first row, end row, n-tile}; *n_tiles = sum_e c_e * ntn.
+__global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets, int E, int bm,
+                                                            int ntn, int4* __restrict__ tiles,
+                                                            int* __restrict__ n_tiles) {
   __shared__ int scan[1024];
   const int e = threadIdx.x;
   int lo = 0, hi = 0, cnt = 0;
@@ -240,9 +247,13 @@ __global__ __launch_bounds__(1024) void build_mtiles_kernel(const int32_t* __res
     scan[e] += v;
     __syncthreads();
   }
-  const int base = scan[e] - cnt;
-  for (int i = 0; i < cnt; ++i) tiles[base + i] = make_int4(e, lo + i * bm, min(hi, lo + (i + 1) * bm), 0);
-  if (e == 1023) *n_tiles = scan[1023];
+  const int base = (scan[e] - cnt) * ntn;
+  const int n = hi - lo;
+  for (int nt = 0; nt < ntn; ++nt)
+    for (int i = 0; i < cnt; ++i)
+      tiles[base + nt * cnt + i] =
+          make_int4(e, lo + (int)((int64_t)i * n / cnt), lo + (int)((int64_t)(i + 1) * n / cnt), nt);
+  if (e == 1023) *n_tiles = scan[1023] * ntn;
 }
 
 // ---------------------------------------------------------------- launch ---
@@ -265,20 +276,51 @@ static hipError_t launch_cfg(const GemmParams& p, int grid_m, hipStream_t s) {
   return hipGetLastError();
 }
 
-GemmShape gemm_shape(int kind, int rows_hint, int n_groups) {
-  (void)n_groups;
+// Tile shapes (kind: WMxWN waves, each TMxTN tiles of 32x32 -> BM x BN):
+//   0: 2x2 waves, 2x2 tiles -> 128 x 128      1: 1x4 waves, 1x2 tiles ->  32 x 256
+//   2: 2x2 waves, 4x4 tiles -> 256 x 256      3: 2x2 waves, 4x2 tiles -> 256 x 128
+//   4: 2x2 waves, 2x4 tiles -> 128 x 256      5: 1x4 waves, 2x2 tiles ->  64 x 256
+#ifndef MOE_TILE_GEMM1
+#define MOE_TILE_GEMM1 -1
+#endif
+#ifndef MOE_TILE_GEMM2
+#define MOE_TILE_GEMM2 -1
+#endif
+static const int kTileBM[6] = {128, 32, 256, 256, 128, 64};
+static const int kTileBN[6] = {128, 256, 256, 128, 256, 256};
+// pipelined kernels (bf16 only): 10, 11: 256 x 256; 12, 13: 128 x 256; 14: 64 x 256
+static int tile_bm(int kind) { return kind >= 10 ? (kind <= 11 ? 256 : kind <= 13 ? 128 : 64) : kTileBM[kind]; }
+static int tile_bn(int kind) { return kind >= 10 ? 256 : kTileBN[kind]; }
+
+// which: 0 = gate/up GEMM, 1 = down GEMM, 2 = router GEMM.  rows_hint = mean
+// rows per group; a_bytes / b_bytes = sizes of the activation buffer and of one
+// group's weights (the pipelined kernel addresses both with 31-bit offsets).
+GemmShape gemm_shape(int which, int dt, int rows_hint, int64_t a_bytes, int64_t b_bytes) {
+  int kind;
+  if (which == 2) kind = 0;
+  else if (rows_hint <= 32) kind = 1;
+  else kind = dt == MOE_DT_BF16 ? 10 : 0;
+  const bool pipe_ok = dt == MOE_DT_BF16 && a_bytes < (1LL << 31) && b_bytes < (1LL << 31);
+  if (which == 0 && MOE_TILE_GEMM1 >= 0) kind = MOE_TILE_GEMM1;
+  if (which == 1 && MOE_TILE_GEMM2 >= 0) kind = MOE_TILE_GEMM2;
+  if (kind >= 10 && !pipe_ok) kind = 0;
   GemmShape g;
-  // Small row counts per group (decode): one 32-row block, waves spread over N.
-  if (rows_hint <= 32) { g.bm = 32; g.bn = 256; g.kind = 1; }
-  else { g.bm = 128; g.bn = 128; g.kind = 0; }
-  (void)kind;
+  g.kind = kind;
+  g.bm = tile_bm(kind);
+  g.bn = tile_bn(kind);
   return g;
 }
 
 template <int DT, int EPI, int ODT>
 static hipError_t dispatch_shape(const GemmParams& p, const GemmShape& g, int grid_m, hipStream_t s) {
-  if (g.kind == 1) return launch_cfg<DT, 1, 4, 1, 2, EPI, ODT>(p, grid_m, s);
-  return launch_cfg<DT, 2, 2, 2, 2, EPI, ODT>(p, grid_m, s);
+  switch (g.kind) {
+    case 1: return launch_cfg<DT, 1, 4, 1, 2, EPI, ODT>(p, grid_m, s);
+    case 2: return launch_cfg<DT, 2, 2, 4, 4, EPI, ODT>(p, grid_m, s);
+    case 3: return launch_cfg<DT, 2, 2, 4, 2, EPI, ODT>(p, grid_m, s);
+    case 4: return launch_cfg<DT, 2, 2, 2, 4, EPI, ODT>(p, grid_m, s);
+    case 5: return launch_cfg<DT, 1, 4, 2, 2, EPI, ODT>(p, grid_m, s);
+    default: return launch_cfg<DT, 2, 2, 2, 2, EPI, ODT>(p, grid_m, s);
+  }
 }
 
 template <int DT, int EPI>
@@ -289,6 +331,10 @@ static hipError_t dispatch_odt(const GemmParams& p, const GemmShape& g, int odt,
 
 hipError_t launch_gemm(int dt, int epi, int odt, const GemmParams& p, const GemmShape& g, int grid_m,
                        hipStream_t s) {
+  if (g.kind >= 10) {
+    if (dt != MOE_DT_BF16) return hipErrorInvalidValue;
+    return launch_gemm_pipe(epi, odt, p, g, grid_m, s);
+  }
   if (dt == MOE_DT_BF16) {
     switch (epi) {
       case EPI_STORE: return dispatch_odt<MOE_DT_BF16, EPI_STORE>(p, g, odt, grid_m, s);
@@ -305,8 +351,9 @@ hipError_t launch_gemm(int dt, int epi, int odt, const GemmParams& p, const Gemm
   }
 }
 
-hipError_t launch_build_mtiles(const int32_t* offsets, int E, int bm, int4* tiles, int* n_tiles, hipStream_t s) {
-  hipLaunchKernelGGL(build_mtiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm, tiles, n_tiles);
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int bm, int ntn, int4* tiles, int* n_tiles,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm, ntn, tiles, n_tiles);
   return hipGetLastError();
 }
 

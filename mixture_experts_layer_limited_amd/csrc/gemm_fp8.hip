@@ -43,17 +43,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_kernel(GemmFp8Params p)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
-  const int total_m = p.tiles ? *p.n_mtiles_dev : p.n_mtiles;
-  const int total = total_m * p.ntn;
+  // device list: every (m-tile, n-tile) pair; dense: n_mtiles x ntn tiles
+  const int total = p.tiles ? *p.n_mtiles_dev : p.n_mtiles * p.ntn;
   const int P = blockIdx.x;
   if (P >= total) return;
   const int L = xcd_remap(P, total);
-  const int mt = L / p.ntn, nt = L - mt * p.ntn;
-  int grp, r0, r1;
+  int grp, r0, r1, nt;
   if (p.tiles) {
-    const int4 t = p.tiles[mt];
-    grp = t.x; r0 = t.y; r1 = t.z;
+    const int4 t = p.tiles[L];
+    grp = t.x; r0 = t.y; r1 = t.z; nt = t.w;
   } else {
+    const int mt = L / p.ntn;
+    nt = L - mt * p.ntn;
     grp = 0; r0 = mt * BM; r1 = min(p.M, r0 + BM);
   }
   const int rows = r1 - r0;

@@ -1,0 +1,313 @@
+// Pipelined grouped bf16 GEMM for the large expert GEMMs (gate/up with the
+// SiLU*up epilogue, down with the row-store or weighted scatter-add epilogue).
+//
+// C[p, n] = sum_k A[src(p), k] * B[g][n, k] over the rows p of m-tile (g, r0, r1)
+//
+// Each K step stages BK = 32 bf16 (64 bytes) of every A row and every B row in
+// one slot of an S-slot LDS ring.  Slots are filled straight from memory by
+// buffer_load ... lds (no register staging), S-1 steps ahead of the MFMAs, so
+// several steps of weight traffic are in flight per CU while the matrix cores
+// work; an explicit "s_waitcnt vmcnt(n); s_barrier" per step releases exactly
+// the slot that is about to be read.  A 16-byte chunk c of row r sits at chunk
+// c ^ (((r >> 1) ^ (r >> 3)) & 3) of its 64-byte LDS row, which keeps the 128-bit
+// fragment reads of 8 (and of 16) consecutive rows on distinct banks.
+//
+// Work-group: 2 x 2 waves, each owning TM row blocks and TN column blocks of
+// 32 (v_mfma_f32_32x32x16_bf16).  Wave row wm takes row blocks wm, wm+2, ...
+// so the two wave rows stay balanced when the tile has fewer live rows than
+// BM; row blocks without live rows issue no MFMAs.  Rows are gathered through
+// permuted_src by the per-lane buffer offsets, so the permuted copy of the
+// activations is never written.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+// 16 bytes per lane from a buffer straight into LDS at dst + 16 * lane.  Kept
+// out of the kernel templates: the host pass drops a kernel template whose body
+// names this builtin.
+__device__ __attribute__((always_inline)) inline void dma16(__amdgpu_buffer_rsrc_t r, lds_char* dst, uint32_t voff,
+                                                            uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes >= 0x7fffffffLL ? 0x7fffffff : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+// Wait until at most n vector-memory operations of this wave are in flight,
+// then meet the other waves at the barrier.  The asm block is also a compiler
+// barrier for memory operations.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// XOR swizzle of the 16-byte chunk index of row r: conflict-free 128-bit reads
+// of 8 and of 16 consecutive rows at one logical chunk.
+template <int ROW>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (ROW == 64) return ((r >> 1) ^ (r >> 3)) & 3;
+  else return (r & 7) ^ ((r >> 3) & 1);
+}
+
+__device__ __forceinline__ float silu_mul_p(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+template <int TM, int TN, int S, int OCC, int ROWB, int EPI, int ODT>
+__global__ __launch_bounds__(256, OCC) void gemm_pipe_kernel(GemmParams p) {
+  constexpr int WM = 2, WN = 2, NW = 4, NT = 256;
+  constexpr int BM = WM * TM * 32;
+  constexpr int BN = WN * TN * 32;
+  constexpr int ROW = ROWB;                     // bytes of K per row per slot (64 or 128)
+  constexpr int CPR = ROW / 16;                 // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;                 // rows per DMA instruction (1 KB)
+  constexpr int NSUB = ROW / 32;                // k16 MFMA sub-steps per slot
+  constexpr int SLOT = (BM + BN) * ROW;         // bytes per ring slot
+  constexpr int AI = BM / RPI / NW;             // DMA instructions per wave per slot
+  constexpr int BI = BN / RPI / NW;
+  constexpr int LI = AI + BI;
+  static_assert(ROW == 64 || ROW == 128, "row bytes");
+  static_assert(AI * RPI * NW == BM && BI * RPI * NW == BN, "tile / wave mismatch");
+  static_assert(EPI != EPI_SWIGLU || TN % 2 == 0, "SwiGLU pairs gate and up tiles");
+  static_assert(S >= 2 && S <= 6, "ring depth");
+
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  lds_char* const lds3 = (lds_char*)lds;  // the same memory as an LDS-address-space pointer
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  // device list: every (m-tile, n-tile) pair; dense: n_mtiles x ntn tiles
+  const int total = p.tiles ? *p.n_mtiles_dev : p.n_mtiles * p.ntn;
+  const int P = blockIdx.x;
+  if (P >= total) return;
+  const int L = xcd_remap(P, total);
+  int grp, r0, r1, nt;
+  if (p.tiles) {
+    const int4 t = p.tiles[L];
+    grp = t.x; r0 = t.y; r1 = t.z; nt = t.w;
+  } else {
+    const int mt = L / p.ntn;
+    nt = L - mt * p.ntn;
+    grp = 0; r0 = mt * BM; r1 = min(p.M, r0 + BM);
+  }
+  const int rows = r1 - r0;
+  const int64_t krow = (int64_t)p.K * 2;  // bytes per A / B row
+  const char* Bg = (const char*)p.B + (int64_t)grp * p.b_gstride * 2;
+  const int b_nrows = (EPI == EPI_SWIGLU) ? 2 * p.N : p.N;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, p.a_nrows * krow);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bg, (int64_t)b_nrows * krow);
+
+  // Per-lane byte offsets of the rows this lane copies (fixed over K).
+  // Lane l of a DMA instruction fills row (l / CPR), slot (l % CPR) of an RPI-row block.
+  const int lrow = lane / CPR, lslot = lane % CPR;
+  uint32_t voa[AI], vob[BI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int r = (wave * AI + i) * RPI + lrow;
+    const int chunk = lslot ^ swz<ROW>(r);
+    const int rr = r < rows ? r : 0;  // rows past the tile read row 0 (results discarded)
+    const int src = p.a_rows ? p.a_rows[r0 + rr] : r0 + rr;
+    voa[i] = (uint32_t)((int64_t)src * krow + chunk * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const int r = (wave * BI + i) * RPI + lrow;
+    const int chunk = lslot ^ swz<ROW>(r);
+    int wrow;
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int j = min(nt * (BN / 2) + (r % (BN / 2)), p.N - 1);
+      wrow = (r < BN / 2) ? j : p.N + j;
+    } else {
+      wrow = min(nt * BN + r, p.N - 1);
+    }
+    vob[i] = (uint32_t)((int64_t)wrow * krow + chunk * 16);
+  }
+
+  const int nk = p.K * 2 / ROW;
+
+  // Issue the DMA of K step kt into ring slot kt % S.  (A macro, not a lambda:
+  // device-only builtins inside a lambda would hide the kernel from the host pass.)
+#define MOE_PIPE_ISSUE(kt_)                                                                        \
+  do {                                                                                             \
+    lds_char* slot_ = lds3 + ((kt_) % S) * SLOT;                                                   \
+    const uint32_t soff_ = (uint32_t)(kt_) * ROW;                                                  \
+    _Pragma("unroll") for (int i = 0; i < AI; ++i)                                                 \
+      dma16(ra, slot_ + (wave * AI + i) * 1024, voa[i], soff_);                                    \
+    _Pragma("unroll") for (int i = 0; i < BI; ++i)                                                 \
+      dma16(rb, slot_ + BM * ROW + (wave * BI + i) * 1024, vob[i], soff_);                         \
+  } while (0)
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  int tm_live = 0;  // row blocks wm, wm+2, ... that hold live rows
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+    if ((wm + 2 * i) * 32 < rows) tm_live = i + 1;
+  tm_live = __builtin_amdgcn_readfirstlane(tm_live);  // wave-uniform: scalar branches only
+
+  auto bblock = [&](int tn) {
+    if constexpr (EPI == EPI_SWIGLU)
+      return tn < TN / 2 ? wn * (TN / 2) + tn : WN * (TN / 2) + wn * (TN / 2) + (tn - TN / 2);
+    else
+      return wn * TN + tn;
+  };
+
+  const int lr = lane & 31, hi = lane >> 5;
+  // (row & 15) == (lr & 15) for every row block, whose starts are multiples of 32
+  const int sw = swz<ROW>(lr);
+
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) MOE_PIPE_ISSUE(s);
+
+  // The K loop on the first NL row blocks of this wave; branch-free inside so the
+  // accumulators stay in place.  Tiles with at most half their row blocks live
+  // run the NL = TM/2 copy.
+#define MOE_PIPE_KLOOP                                                                              \
+  for (int kt = 0; kt < nk; ++kt) {                                                                 \
+    /* slot kt is complete once at most (DMAs issued after kt) are pending */                       \
+    const int ahead = min(S - 2, nk - 1 - kt);                                                      \
+    if (ahead >= S - 2) wait_vm_barrier<(S - 2) * LI>();                                            \
+    else if (ahead == 3) wait_vm_barrier<3 * LI>();                                                 \
+    else if (ahead == 2) wait_vm_barrier<2 * LI>();                                                 \
+    else if (ahead == 1) wait_vm_barrier<1 * LI>();                                                 \
+    else wait_vm_barrier<0>();                                                                      \
+    if (kt + S - 1 < nk) MOE_PIPE_ISSUE(kt + S - 1);                                                \
+    const char* slot = lds + (kt % S) * SLOT;                                                       \
+    u32x4 a[NSUB][NL], b[NSUB][TN];                                                                 \
+    _Pragma("unroll") for (int st = 0; st < NSUB; ++st) {                                           \
+      const int coff = ((2 * st + hi) ^ sw) * 16;                                                   \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                \
+        b[st][j] = *(const u32x4*)(slot + BM * ROW + (bblock(j) * 32 + lr) * ROW + coff);           \
+      _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                \
+        a[st][i] = *(const u32x4*)(slot + ((wm + 2 * i) * 32 + lr) * ROW + coff);                   \
+    }                                                                                               \
+    _Pragma("unroll") for (int st = 0; st < NSUB; ++st)                                             \
+      _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j)                                              \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[st][i]), \
+                                                              __builtin_bit_cast(bf16x8, b[st][j]), \
+                                                              acc[i][j], 0, 0, 0);                  \
+    /* schedule: the first sub-step's fragment reads, then its MFMAs with the second */             \
+    /* sub-step's reads spread among them, then the remaining MFMAs */                              \
+    __builtin_amdgcn_sched_group_barrier(0x100, NL + TN, 0);                                        \
+    _Pragma("unroll") for (int q = 0; q < NL + TN; ++q) {                                           \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                            \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                            \
+    }                                                                                               \
+    __builtin_amdgcn_sched_group_barrier(0x008, REST, 0);                                           \
+    _Pragma("unroll") for (int st = 2; st < NSUB; ++st) {                                           \
+      _Pragma("unroll") for (int q = 0; q < NL + TN; ++q) {                                         \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                          \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                          \
+      }                                                                                             \
+      __builtin_amdgcn_sched_group_barrier(0x008, REST, 0);                                         \
+    }                                                                                               \
+    __builtin_amdgcn_sched_group_barrier(0x008, NL * TN, 0);                                        \
+  }
+
+  constexpr int HALF = TM / 2 > 0 ? TM / 2 : 1;
+  if (TM > 1 && tm_live <= HALF) {
+    constexpr int NL = HALF;
+    constexpr int REST = NL * TN > NL + TN ? NL * TN - (NL + TN) : 0;
+    MOE_PIPE_KLOOP
+  } else {
+    constexpr int NL = TM;
+    constexpr int REST = NL * TN > NL + TN ? NL * TN - (NL + TN) : 0;
+    MOE_PIPE_KLOOP
+  }
+#undef MOE_PIPE_KLOOP
+#undef MOE_PIPE_ISSUE
+
+  // Epilogue.  Lane l, register e of a 32x32 block: row 8*(e/4) + 4*(l/32) + e%4, column l%32.
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    if (i >= tm_live) continue;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = (wm + 2 * i) * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+      if (row >= rows) continue;
+      const int prow = r0 + row;
+      if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int j = 0; j < TN / 2; ++j) {
+          const int col = nt * (BN / 2) + (wn * (TN / 2) + j) * 32 + lr;
+          if (col < p.N)
+            Elem<ODT>::store((typename Elem<ODT>::T*)p.C, (int64_t)prow * p.N + col,
+                             silu_mul_p(acc[i][j][e], acc[i][j + TN / 2][e]));
+        }
+      } else if constexpr (EPI == EPI_SCATTER) {
+        const int tok = p.c_rows ? p.c_rows[prow] : prow;
+        const float w = p.row_w[prow];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = nt * BN + bblock(j) * 32 + lr;
+          if (col < p.N) atomicAdd((float*)p.C + (int64_t)tok * p.N + col, w * acc[i][j][e]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = nt * BN + bblock(j) * 32 + lr;
+          if (col < p.N) Elem<ODT>::store((typename Elem<ODT>::T*)p.C, (int64_t)prow * p.N + col, acc[i][j][e]);
+        }
+      }
+    }
+  }
+}
+
+template <int TM, int TN, int S, int OCC, int ROWB, int EPI, int ODT>
+static hipError_t launch_pipe(const GemmParams& p, int grid_m, hipStream_t s) {
+  constexpr int BM = 2 * TM * 32, BN = 2 * TN * 32;
+  constexpr int lds_bytes = S * (BM + BN) * ROWB;
+  static_assert(lds_bytes * OCC <= 160 * 1024, "LDS");
+  auto kern = gemm_pipe_kernel<TM, TN, S, OCC, ROWB, EPI, ODT>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t grid = (int64_t)grid_m * p.ntn;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds_bytes, s, p);
+  return hipGetLastError();
+}
+
+// kind 10: 256 x 256, 64-byte rows, 4-slot ring, one work-group per CU
+// kind 11: 256 x 256, 128-byte rows, 2-slot ring, one work-group per CU
+// kind 12: 128 x 256, 128-byte rows, 3-slot ring, one work-group per CU
+// kind 13: 128 x 256, 64-byte rows, 5-slot ring, one work-group per CU
+// kind 14:  64 x 256, 128-byte rows, 4-slot ring, one work-group per CU
+template <int EPI, int ODT>
+static hipError_t pipe_kind(const GemmParams& p, const GemmShape& g, int grid_m, hipStream_t s) {
+  switch (g.kind) {
+    case 11: return launch_pipe<4, 4, 2, 1, 128, EPI, ODT>(p, grid_m, s);
+    case 12: return launch_pipe<2, 4, 3, 1, 128, EPI, ODT>(p, grid_m, s);
+    case 13: return launch_pipe<2, 4, 5, 1, 64, EPI, ODT>(p, grid_m, s);
+    case 14: return launch_pipe<1, 4, 4, 1, 128, EPI, ODT>(p, grid_m, s);
+    default: return launch_pipe<4, 4, 4, 1, 64, EPI, ODT>(p, grid_m, s);
+  }
+}
+
+hipError_t launch_gemm_pipe(int epi, int odt, const GemmParams& p, const GemmShape& g, int grid_m, hipStream_t s) {
+  switch (epi) {
+    case EPI_SWIGLU: return pipe_kind<EPI_SWIGLU, MOE_DT_BF16>(p, g, grid_m, s);
+    case EPI_SCATTER: return pipe_kind<EPI_SCATTER, MOE_DT_F32>(p, g, grid_m, s);
+    default:
+      if (odt == MOE_DT_F32) return pipe_kind<EPI_STORE, MOE_DT_F32>(p, g, grid_m, s);
+      return pipe_kind<EPI_STORE, MOE_DT_BF16>(p, g, grid_m, s);
+  }
+}
+
+}  // namespace moe

@@ -20,11 +20,12 @@ struct GemmParams {
   void* C;                // output: rows p (store, SwiGLU) or rows c_rows[p] (scatter)
   const int32_t* c_rows;  // scatter: output row of row p; NULL: p
   const float* row_w;     // scatter: weight of row p
-  const int4* tiles;      // m-tiles {group, row0, row1, -}; NULL: dense rows [0, M)
-  const int* n_mtiles_dev;
+  const int4* tiles;      // tiles {group, row0, row1, n-tile}; NULL: dense rows [0, M)
+  const int* n_mtiles_dev; // number of entries of `tiles`
   int n_mtiles;           // dense: number of m-tiles
   int M;                  // dense: rows
   int ntn;                // number of n-tiles
+  int64_t a_nrows;        // rows of A (bounds of the activation buffer)
 };
 
 struct GemmShape {
@@ -33,11 +34,13 @@ struct GemmShape {
   int kind = 0;
 };
 
-GemmShape gemm_shape(int kind, int rows_hint, int n_groups);
+GemmShape gemm_shape(int which, int dt, int rows_hint, int64_t a_bytes, int64_t b_bytes);
 hipError_t launch_gemm(int dt, int epi, int odt, const GemmParams& p, const GemmShape& g, int grid_m,
                        hipStream_t s);
-hipError_t launch_build_mtiles(const int32_t* offsets, int E, int bm, int4* tiles, int* n_tiles,
-                               hipStream_t s);
+// Pipelined bf16 kernel (LDS ring filled by direct-to-LDS buffer loads).
+hipError_t launch_gemm_pipe(int epi, int odt, const GemmParams& p, const GemmShape& g, int grid_m, hipStream_t s);
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int bm, int ntn, int4* tiles, int* n_tiles,
+                              hipStream_t s);
 
 // FP8 grouped GEMM: A = E4M3 codes with 1x128 fp32 scales, B = E4M3 codes with
 // 128x128 fp32 block scales.
