@@ -298,8 +298,8 @@ static int tile_bn(int kind) { return kind >= 10 ? 256 : kTileBN[kind]; }
 GemmShape gemm_shape(int which, int dt, int rows_hint, int64_t a_bytes, int64_t b_bytes) {
   int kind;
   if (which == 2) kind = 0;
-  else if (rows_hint <= 32) kind = 1;
-  else kind = dt == MOE_DT_BF16 ? 10 : 0;
+  else if (rows_hint <= 32) kind = dt == MOE_DT_BF16 ? 14 : 1;
+  else kind = dt == MOE_DT_BF16 ? 12 : 0;
   const bool pipe_ok = dt == MOE_DT_BF16 && a_bytes < (1LL << 31) && b_bytes < (1LL << 31);
   if (which == 0 && MOE_TILE_GEMM1 >= 0) kind = MOE_TILE_GEMM1;
   if (which == 1 && MOE_TILE_GEMM2 >= 0) kind = MOE_TILE_GEMM2;

@@ -55,6 +55,25 @@ __device__ __forceinline__ int swz(int r) {
   else return (r & 7) ^ ((r >> 3) & 1);
 }
 
+template <int Q, int M, int LI>
+__device__ __forceinline__ void pipe_schedule_mfmas() {
+  if constexpr (Q < M) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    constexpr int DE = M / LI > 0 ? M / LI : 1;         // a ring DMA after every DE MFMAs
+    if constexpr (LI > 0 && (Q + 1) % DE == 0 && (Q + 1) / DE <= LI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    pipe_schedule_mfmas<Q + 1, M, LI>();
+  }
+}
+
+// Instruction order of one K step (a hint to the scheduler): all fragment reads
+// of the step, then the MFMAs with the ring DMAs spread evenly among them, so
+// the DMAs reach the address unit one at a time while the matrix cores are busy.
+template <int NL, int TN, int NSUB, int LI>
+__device__ __forceinline__ void pipe_schedule() {
+  __builtin_amdgcn_sched_group_barrier(0x100, NSUB * (NL + TN), 0);
+  pipe_schedule_mfmas<0, NSUB * NL * TN, LI>();
+}
+
 __device__ __forceinline__ float silu_mul_p(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
 template <int TM, int TN, int S, int OCC, int ROWB, int EPI, int ODT>
@@ -78,7 +97,8 @@ __global__ __launch_bounds__(256, OCC) void gemm_pipe_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   lds_char* const lds3 = (lds_char*)lds;  // the same memory as an LDS-address-space pointer
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
   const int wm = wave / WN, wn = wave % WN;
 
   // device list: every (m-tile, n-tile) pair; dense: n_mtiles x ntn tiles
@@ -130,12 +150,15 @@ __global__ __launch_bounds__(256, OCC) void gemm_pipe_kernel(GemmParams p) {
 
   const int nk = p.K * 2 / ROW;
 
-  // Issue the DMA of K step kt into ring slot kt % S.  (A macro, not a lambda:
-  // device-only builtins inside a lambda would hide the kernel from the host pass.)
+  // Issue the DMA of K step kt into ring slot kt % S; for kt >= nk the offset is
+  // out of the buffers' range, so the hardware writes zeros without touching
+  // memory (keeps the loop body branch-free and the vmcnt bookkeeping constant).
+  // (A macro, not a lambda: device-only builtins inside a lambda would hide the
+  // kernel from the host pass.)
 #define MOE_PIPE_ISSUE(kt_)                                                                        \
   do {                                                                                             \
     lds_char* slot_ = lds3 + ((kt_) % S) * SLOT;                                                   \
-    const uint32_t soff_ = (uint32_t)(kt_) * ROW;                                                  \
+    const uint32_t soff_ = (kt_) < nk ? (uint32_t)(kt_) * ROW : 0x80000000u;                       \
     _Pragma("unroll") for (int i = 0; i < AI; ++i)                                                 \
       dma16(ra, slot_ + (wave * AI + i) * 1024, voa[i], soff_);                                    \
     _Pragma("unroll") for (int i = 0; i < BI; ++i)                                                 \
@@ -168,22 +191,15 @@ __global__ __launch_bounds__(256, OCC) void gemm_pipe_kernel(GemmParams p) {
   const int sw = swz<ROW>(lr);
 
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s)
-    if (s < nk) MOE_PIPE_ISSUE(s);
+  for (int s = 0; s < S - 1; ++s) MOE_PIPE_ISSUE(s);
 
   // The K loop on the first NL row blocks of this wave; branch-free inside so the
   // accumulators stay in place.  Tiles with at most half their row blocks live
   // run the NL = TM/2 copy.
 #define MOE_PIPE_KLOOP                                                                              \
   for (int kt = 0; kt < nk; ++kt) {                                                                 \
-    /* slot kt is complete once at most (DMAs issued after kt) are pending */                       \
-    const int ahead = min(S - 2, nk - 1 - kt);                                                      \
-    if (ahead >= S - 2) wait_vm_barrier<(S - 2) * LI>();                                            \
-    else if (ahead == 3) wait_vm_barrier<3 * LI>();                                                 \
-    else if (ahead == 2) wait_vm_barrier<2 * LI>();                                                 \
-    else if (ahead == 1) wait_vm_barrier<1 * LI>();                                                 \
-    else wait_vm_barrier<0>();                                                                      \
-    if (kt + S - 1 < nk) MOE_PIPE_ISSUE(kt + S - 1);                                                \
+    /* slot kt is complete once at most the S-2 later slots' DMAs are pending */                    \
+    wait_vm_barrier<(S - 2) * LI>();                                                                \
     const char* slot = lds + (kt % S) * SLOT;                                                       \
     u32x4 a[NSUB][NL], b[NSUB][TN];                                                                 \
     _Pragma("unroll") for (int st = 0; st < NSUB; ++st) {                                           \
@@ -193,40 +209,27 @@ __global__ __launch_bounds__(256, OCC) void gemm_pipe_kernel(GemmParams p) {
       _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                \
         a[st][i] = *(const u32x4*)(slot + ((wm + 2 * i) * 32 + lr) * ROW + coff);                   \
     }                                                                                               \
+    /* the ring DMAs go after the fragment reads in program order (they may not */                  \
+    /* pass LDS reads), then spread among the MFMAs */                                              \
+    MOE_PIPE_ISSUE(kt + S - 1);                                                                     \
     _Pragma("unroll") for (int st = 0; st < NSUB; ++st)                                             \
       _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                \
         _Pragma("unroll") for (int j = 0; j < TN; ++j)                                              \
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[st][i]), \
                                                               __builtin_bit_cast(bf16x8, b[st][j]), \
                                                               acc[i][j], 0, 0, 0);                  \
-    /* schedule: the first sub-step's fragment reads, then its MFMAs with the second */             \
-    /* sub-step's reads spread among them, then the remaining MFMAs */                              \
-    __builtin_amdgcn_sched_group_barrier(0x100, NL + TN, 0);                                        \
-    _Pragma("unroll") for (int q = 0; q < NL + TN; ++q) {                                           \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                            \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                            \
-    }                                                                                               \
-    __builtin_amdgcn_sched_group_barrier(0x008, REST, 0);                                           \
-    _Pragma("unroll") for (int st = 2; st < NSUB; ++st) {                                           \
-      _Pragma("unroll") for (int q = 0; q < NL + TN; ++q) {                                         \
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                          \
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                          \
-      }                                                                                             \
-      __builtin_amdgcn_sched_group_barrier(0x008, REST, 0);                                         \
-    }                                                                                               \
-    __builtin_amdgcn_sched_group_barrier(0x008, NL * TN, 0);                                        \
+    pipe_schedule<NL, TN, NSUB, LI>();                                                              \
   }
 
   constexpr int HALF = TM / 2 > 0 ? TM / 2 : 1;
   if (TM > 1 && tm_live <= HALF) {
     constexpr int NL = HALF;
-    constexpr int REST = NL * TN > NL + TN ? NL * TN - (NL + TN) : 0;
     MOE_PIPE_KLOOP
   } else {
     constexpr int NL = TM;
-    constexpr int REST = NL * TN > NL + TN ? NL * TN - (NL + TN) : 0;
     MOE_PIPE_KLOOP
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the tail's zero-fill DMAs
 #undef MOE_PIPE_KLOOP
 #undef MOE_PIPE_ISSUE
 
@@ -284,17 +287,17 @@ static hipError_t launch_pipe(const GemmParams& p, int grid_m, hipStream_t s) {
   return hipGetLastError();
 }
 
-// kind 10: 256 x 256, 64-byte rows, 4-slot ring, one work-group per CU
-// kind 11: 256 x 256, 128-byte rows, 2-slot ring, one work-group per CU
-// kind 12: 128 x 256, 128-byte rows, 3-slot ring, one work-group per CU
-// kind 13: 128 x 256, 64-byte rows, 5-slot ring, one work-group per CU
-// kind 14:  64 x 256, 128-byte rows, 4-slot ring, one work-group per CU
+// kind 10: 256 x 256, 64-byte rows, 4-slot ring
+// kind 11: 256 x 256, 128-byte rows, 2-slot ring
+// kind 12: 128 x 256, 128-byte rows, 3-slot ring
+// kind 13: 128 x 256, 64-byte rows, 6-slot ring
+// kind 14:  64 x 256, 128-byte rows, 4-slot ring
 template <int EPI, int ODT>
 static hipError_t pipe_kind(const GemmParams& p, const GemmShape& g, int grid_m, hipStream_t s) {
   switch (g.kind) {
     case 11: return launch_pipe<4, 4, 2, 1, 128, EPI, ODT>(p, grid_m, s);
     case 12: return launch_pipe<2, 4, 3, 1, 128, EPI, ODT>(p, grid_m, s);
-    case 13: return launch_pipe<2, 4, 5, 1, 64, EPI, ODT>(p, grid_m, s);
+    case 13: return launch_pipe<2, 4, 6, 1, 64, EPI, ODT>(p, grid_m, s);
     case 14: return launch_pipe<1, 4, 4, 1, 128, EPI, ODT>(p, grid_m, s);
     default: return launch_pipe<4, 4, 4, 1, 64, EPI, ODT>(p, grid_m, s);
   }
