@@ -113,6 +113,13 @@ GemmShape shape2(const moe_config* c, int64_t rows, int groups, int I) {
   return gemm_shape(1, act_dt(c), (int)(rows / groups), rows * I * eb, (int64_t)c->hidden * I * eb);
 }
 
+GemmShape fp8_shape1(const moe_config* c, int64_t T, int64_t rows, int groups, int I) {
+  return gemm_fp8_shape((int)(rows / groups), T * c->hidden, (int64_t)2 * I * c->hidden);
+}
+GemmShape fp8_shape2(const moe_config* c, int64_t rows, int groups, int I) {
+  return gemm_fp8_shape((int)(rows / groups), rows * I, (int64_t)c->hidden * I);
+}
+
 // Workspace of one grouped SwiGLU over `rows` permuted rows of `groups` experts
 // with intermediate size I.
 struct SwigluWs {
@@ -126,8 +133,9 @@ struct SwigluWs {
 void carve_swiglu(Carver& cv, const moe_config* c, int64_t T, int64_t rows, int groups, int I,
                   bool quantize_x, bool scatter, SwigluWs& w) {
   const int64_t avg = rows / groups;
-  const GemmShape g1 = is_fp8(c) ? gemm_fp8_shape((int)avg) : shape1(c, T, rows, groups, I);
-  const GemmShape g2 = is_fp8(c) ? gemm_fp8_shape((int)avg) : shape2(c, rows, groups, I);
+  (void)avg;
+  const GemmShape g1 = is_fp8(c) ? fp8_shape1(c, T, rows, groups, I) : shape1(c, T, rows, groups, I);
+  const GemmShape g2 = is_fp8(c) ? fp8_shape2(c, rows, groups, I) : shape2(c, rows, groups, I);
   // tile lists: every (m-tile, n-tile) pair of the gate/up and of the down GEMM
   w.tiles1 = cv.take<int4>((size_t)max_mtiles(rows, g1.bm, groups) * ntiles_n(I, g1.bn / 2) + 1);
   w.ntiles1 = cv.take<int>(1);
@@ -254,12 +262,13 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
       HIP_TRY(launch_quantize(act_dt(c), T, H, hidden, w.xq, w.xs, s));
       xq = w.xq; xs = w.xs;
     }
-    const GemmShape g = gemm_fp8_shape((int)avg);
+    const GemmShape g1 = fp8_shape1(c, T, rows, groups, I);
+    const GemmShape g2 = fp8_shape2(c, rows, groups, I);
     const bool dense = offsets == nullptr;
-    const int ntn1 = ntiles_n(I, g.bn / 2), ntn2 = ntiles_n(H, g.bn);
+    const int ntn1 = ntiles_n(I, g1.bn / 2), ntn2 = ntiles_n(H, g2.bn);
     if (!dense) {
-      HIP_TRY(launch_build_tiles(offsets, groups, g.bm, ntn1, w.tiles1, w.ntiles1, s));
-      HIP_TRY(launch_build_tiles(offsets, groups, g.bm, ntn2, w.tiles2, w.ntiles2, s));
+      HIP_TRY(launch_build_tiles(offsets, groups, g1.bm, ntn1, w.tiles1, w.ntiles1, s));
+      HIP_TRY(launch_build_tiles(offsets, groups, g2.bm, ntn2, w.tiles2, w.ntiles2, s));
     }
     GemmFp8Params p{};
     p.A = xq; p.a_scales = xs; p.a_rows = src;
@@ -267,11 +276,12 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
     p.b_gstride = (int64_t)2 * I * H; p.bs_gstride = (int64_t)(2 * I / 128) * (H / 128);
     p.K = H; p.N = I;
     p.C = w.h;
-    set_tiles(p, dense, rows, g.bm, w.tiles1, w.ntiles1);
+    p.a_nrows = T;
+    set_tiles(p, dense, rows, g1.bm, w.tiles1, w.ntiles1);
     p.ntn = ntn1;
-    const int gm = dense ? p.n_mtiles : max_mtiles(rows, g.bm, groups);
+    const int gm1 = dense ? p.n_mtiles : max_mtiles(rows, g1.bm, groups);
     MOE_TRY(mark(0));
-    HIP_TRY(launch_gemm_fp8(EPI_SWIGLU, p, g, gm, s));
+    HIP_TRY(launch_gemm_fp8(EPI_SWIGLU, p, g1, gm1, s));
     MOE_TRY(mark(1));
     HIP_TRY(launch_quantize(MOE_DT_BF16, rows, I, w.h, w.hq, w.h_scales, s));
     GemmFp8Params q{};
@@ -279,17 +289,19 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
     q.B = (const uint8_t*)w2; q.b_scales = w2_s;
     q.b_gstride = (int64_t)H * I; q.bs_gstride = (int64_t)(H / 128) * (I / 128);
     q.K = I; q.N = H;
-    set_tiles(q, dense, rows, g.bm, w.tiles2, w.ntiles2);
+    q.a_nrows = rows;
+    set_tiles(q, dense, rows, g2.bm, w.tiles2, w.ntiles2);
     q.ntn = ntn2;
+    const int gm2 = dense ? q.n_mtiles : max_mtiles(rows, g2.bm, groups);
     if (epi == MOE_EPI_SCATTER_ADD) {
       HIP_TRY(launch_row_weights(topk_w, inv, (int)rows, w.row_w, s));
       q.C = acc; q.c_rows = src; q.row_w = w.row_w;
       MOE_TRY(mark(2));
-      HIP_TRY(launch_gemm_fp8(EPI_SCATTER, q, g, gm, s));
+      HIP_TRY(launch_gemm_fp8(EPI_SCATTER, q, g2, gm2, s));
     } else {
       q.C = out;
       MOE_TRY(mark(2));
-      HIP_TRY(launch_gemm_fp8(EPI_STORE, q, g, gm, s));
+      HIP_TRY(launch_gemm_fp8(EPI_STORE, q, g2, gm2, s));
     }
     return mark(3);
   }

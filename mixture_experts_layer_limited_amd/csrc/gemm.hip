@@ -288,8 +288,11 @@ static hipError_t launch_cfg(const GemmParams& p, int grid_m, hipStream_t s) {
 #endif
 static const int kTileBM[6] = {128, 32, 256, 256, 128, 64};
 static const int kTileBN[6] = {128, 256, 256, 128, 256, 256};
-// pipelined kernels (bf16 only): 10, 11: 256 x 256; 12, 13: 128 x 256; 14: 64 x 256
-static int tile_bm(int kind) { return kind >= 10 ? (kind <= 11 ? 256 : kind <= 13 ? 128 : 64) : kTileBM[kind]; }
+// pipelined kernels (bf16 only): 10, 11, 15: 256 x 256; 12, 13, 16: 128 x 256; 14: 64 x 256
+static int tile_bm(int kind) {
+  if (kind < 10) return kTileBM[kind];
+  return (kind <= 11 || kind == 15) ? 256 : (kind <= 13 || kind == 16) ? 128 : 64;
+}
 static int tile_bn(int kind) { return kind >= 10 ? 256 : kTileBN[kind]; }
 
 // which: 0 = gate/up GEMM, 1 = down GEMM, 2 = router GEMM.  rows_hint = mean
@@ -299,7 +302,8 @@ GemmShape gemm_shape(int which, int dt, int rows_hint, int64_t a_bytes, int64_t 
   int kind;
   if (which == 2) kind = 0;
   else if (rows_hint <= 32) kind = dt == MOE_DT_BF16 ? 14 : 1;
-  else kind = dt == MOE_DT_BF16 ? 12 : 0;
+  else if (rows_hint < 128) kind = dt == MOE_DT_BF16 ? 12 : 0;
+  else kind = dt == MOE_DT_BF16 ? 15 : 0;
   const bool pipe_ok = dt == MOE_DT_BF16 && a_bytes < (1LL << 31) && b_bytes < (1LL << 31);
   if (which == 0 && MOE_TILE_GEMM1 >= 0) kind = MOE_TILE_GEMM1;
   if (which == 1 && MOE_TILE_GEMM2 >= 0) kind = MOE_TILE_GEMM2;

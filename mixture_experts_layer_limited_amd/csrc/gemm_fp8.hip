@@ -12,6 +12,7 @@
 // m-tile list and the work-group mapping are those of the bf16 kernel.
 #include "common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace moe {
 
@@ -23,6 +24,8 @@ __device__ __forceinline__ f32x16 mma_fp8(const u32x4& a0, const u32x4& a1, cons
   // scales are applied outside the MFMA)
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
+
+typedef __attribute__((address_space(4))) const float cfloat;
 
 __device__ __forceinline__ float silu_mul8(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
@@ -37,8 +40,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_kernel(GemmFp8Params p)
   static_assert(EPI != EPI_SWIGLU || TN % 2 == 0, "SwiGLU pairs gate and up tiles");
   static_assert(BM <= NT, "one activation scale per thread");
   constexpr int STAGE = (BM + BN) * 8;                 // u32x4 per operand stage
-  extern __shared__ u32x4 lds[];
-  float* sa_lds = (float*)(lds + 2 * STAGE);           // [2][BM]
+  extern __shared__ u32x4 lds4[];
+  float* sa_lds = (float*)(lds4 + 2 * STAGE);           // [2][BM]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_kernel(GemmFp8Params p)
   } while (0)
 #define MOE_SSTORE(buf_)                                                     \
   do {                                                                       \
-    u32x4* s_ = lds + (buf_) * STAGE;                                        \
+    u32x4* s_ = lds4 + (buf_) * STAGE;                                        \
     _Pragma("unroll") for (int i = 0; i < CA; ++i) if (aok[i]) s_[aoff[i]] = ra[i]; \
     _Pragma("unroll") for (int i = 0; i < CB; ++i) s_[boff[i]] = rb[i];      \
     if (tid < BM) sa_lds[(buf_) * BM + tid] = sok ? rsa : 0.0f;              \
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_kernel(GemmFp8Params p)
     const int buf = kt & 1;
     if (kt + 1 < nkb) MOE_GLOAD(kt + 1);
     if (tm_live > 0) {
-      const u32x4* s = lds + buf * STAGE;
+      const u32x4* s = lds4 + buf * STAGE;
       float sb[TN];
 #pragma unroll
       for (int j = 0; j < TN; ++j) sb[j] = SBg[(int64_t)sbrow[j] * nkb + kt];
@@ -233,10 +236,320 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_kernel(GemmFp8Params p)
   }
 }
 
-GemmShape gemm_fp8_shape(int rows_hint) {
+// ---------------------------------------------------------------------------
+// Pipelined FP8 kernel.  One K step = one 128-wide scale block = 128 bytes of
+// every A and B row, streamed straight into LDS rings (A: SA slots, B: SB slots)
+// by buffer_load ... lds, as in the bf16 split-ring kernel.  The A slot also
+// carries the step's activation scales of the tile's rows (one 4-byte DMA lane
+// per row).  Weight-block scales are wave-uniform scalar loads, fetched one step
+// ahead.  Per step and 32x32 block: two 32x32x64 MFMAs into a zeroed partial,
+// then acc += partial * (sa[row] * sb).
+template <int TM, int TN, int SA, int SB, int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_fp8_split_kernel(GemmFp8Params p) {
+  constexpr int WM = 2, WN = 2, NW = 4;
+  constexpr int BM = WM * TM * 32;
+  constexpr int BN = WN * TN * 32;
+  constexpr int ROW = 128, CPR = 8, RPI = 8;
+  constexpr int ADATA = BM * ROW;
+  constexpr int ASLOT = ADATA + NW * 256;     // + activation scales: 64 lanes x 4 B per wave
+  constexpr int BSLOT = BN * ROW;
+  constexpr int AI = BM / RPI / NW, BI = BN / RPI / NW;
+  constexpr int RW = BM / NW;                 // scale rows per wave (32 or 64)
+  constexpr int AL = AI + 1;                  // A instructions per wave per step (data + scales)
+  constexpr int LI = AL + BI;
+  constexpr int VMN = SB > SA ? BI + (SA - 2) * LI : (SA - 2) * LI;
+  static_assert(AI * RPI * NW == BM && BI * RPI * NW == BN, "tile / wave mismatch");
+  static_assert(RW == 32 || RW == 64, "scale rows per wave");
+  static_assert(SA >= 2 && SB >= SA && VMN < 64, "ring depths");
+  static_assert(EPI != EPI_SWIGLU || TN % 2 == 0, "SwiGLU pairs gate and up tiles");
+
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  lds_char* const lds3 = (lds_char*)lds;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+
+  const int total = p.tiles ? *p.n_mtiles_dev : p.n_mtiles * p.ntn;
+  const int P = blockIdx.x;
+  if (P >= total) return;
+  const int L = xcd_remap(P, total);
+  int grp, r0, r1, nt;
+  if (p.tiles) {
+    const int4 t = p.tiles[L];
+    grp = t.x; r0 = t.y; r1 = t.z; nt = t.w;
+  } else {
+    const int mt = L / p.ntn;
+    nt = L - mt * p.ntn;
+    grp = 0; r0 = mt * BM; r1 = min(p.M, r0 + BM);
+  }
+  const int rows = r1 - r0;
+  const int64_t krow = p.K;  // bytes per A / B row
+  const int nkb = p.K / 128;
+  const uint8_t* Bg = p.B + (int64_t)grp * p.b_gstride;
+  // weight scales are read-only for the kernel's lifetime: constant address
+  // space, so the wave-uniform loads below become scalar loads
+  const cfloat* SBg = (const cfloat*)(p.b_scales + (int64_t)grp * p.bs_gstride);
+  const int b_nrows = (EPI == EPI_SWIGLU) ? 2 * p.N : p.N;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, p.a_nrows * krow);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.a_scales, p.a_nrows * nkb * 4);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bg, (int64_t)b_nrows * krow);
+
+  const int lrow = lane / CPR, lslot = lane % CPR;
+  uint32_t voa[AI], vob[BI], vos;
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int r = (wave * AI + i) * RPI + lrow;
+    const int chunk = lslot ^ swz<ROW>(r);
+    if (r < rows) {
+      const int src = p.a_rows ? p.a_rows[r0 + r] : r0 + r;
+      voa[i] = (uint32_t)((int64_t)src * krow + chunk * 16);
+    } else {
+      voa[i] = 0x40000000u;
+    }
+  }
+  {
+    const int r = wave * RW + lane;  // lanes past RW fill the wave's spare scale words
+    if (lane < RW && r < rows) {
+      const int src = p.a_rows ? p.a_rows[r0 + r] : r0 + r;
+      vos = (uint32_t)((int64_t)src * nkb * 4);
+    } else {
+      vos = 0x40000000u;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const int r = (wave * BI + i) * RPI + lrow;
+    const int chunk = lslot ^ swz<ROW>(r);
+    int wrow;
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int j = min(nt * (BN / 2) + (r % (BN / 2)), p.N - 1);
+      wrow = (r < BN / 2) ? j : p.N + j;
+    } else {
+      wrow = min(nt * BN + r, p.N - 1);
+    }
+    vob[i] = (uint32_t)((int64_t)wrow * krow + chunk * 16);
+  }
+
+  auto bblock = [&](int tn) {
+    if constexpr (EPI == EPI_SWIGLU)
+      return tn < TN / 2 ? wn * (TN / 2) + tn : WN * (TN / 2) + wn * (TN / 2) + (tn - TN / 2);
+    else
+      return wn * TN + tn;
+  };
+  // weight-block row (of 128 output rows) of each wave column block
+  int sbrow[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int bb = bblock(j) * 32;
+    int wrow;
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int j0 = min(nt * (BN / 2) + (bb % (BN / 2)), p.N - 1);
+      wrow = (bb < BN / 2) ? j0 : p.N + j0;
+    } else {
+      wrow = min(nt * BN + bb, p.N - 1);
+    }
+    sbrow[j] = __builtin_amdgcn_readfirstlane(wrow / 128);
+  }
+
+  const int nk = nkb;
+  lds_char* const ring_a = lds3;
+  lds_char* const ring_b = lds3 + SA * ASLOT;
+
+#define MOE_F8_ISSUE_A(kt_, lo_, hi_, scales_)                                         \
+  do {                                                                                 \
+    lds_char* slot_ = ring_a + ((kt_) % SA) * ASLOT;                                   \
+    const uint32_t soff_ = (kt_) < nk ? (uint32_t)(kt_) * ROW : 0x80000000u;           \
+    _Pragma("unroll") for (int i = (lo_); i < (hi_); ++i)                              \
+      dma16(ra, slot_ + (wave * AI + i) * 1024, voa[i], soff_);                        \
+    if (scales_) {                                                                     \
+      const uint32_t so4_ = (kt_) < nk ? (uint32_t)(kt_) * 4 : 0x80000000u;            \
+      dma4(rs, slot_ + ADATA + wave * 256, vos, so4_);                                 \
+    }                                                                                  \
+  } while (0)
+#define MOE_F8_ISSUE_B(kt_, lo_, hi_)                                                  \
+  do {                                                                                 \
+    lds_char* slot_ = ring_b + ((kt_) % SB) * BSLOT;                                   \
+    const uint32_t soff_ = (kt_) < nk ? (uint32_t)(kt_) * ROW : 0x80000000u;           \
+    _Pragma("unroll") for (int i = (lo_); i < (hi_); ++i)                              \
+      dma16(rb, slot_ + (wave * BI + i) * 1024, vob[i], soff_);                        \
+  } while (0)
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  int tm_live = 0;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+    if ((wm + 2 * i) * 32 < rows) tm_live = i + 1;
+  tm_live = __builtin_amdgcn_readfirstlane(tm_live);
+
+  const int lr = lane & 31, hi = lane >> 5;
+  const int sw = swz<ROW>(lr);
+
+#pragma unroll
+  for (int v = 1 - SB; v < 0; ++v) {
+    if (v + SA - 1 >= 0) MOE_F8_ISSUE_A(v + SA - 1, 0, AI, true);
+    if (v + SB - 1 >= 0) MOE_F8_ISSUE_B(v + SB - 1, 0, BI);
+  }
+
+  // weight-block scales of step 0; each step fetches the next step's
+  float sbn[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) sbn[j] = SBg[(int64_t)sbrow[j] * nkb];
+
+  // Fragment of sub-step st (K 64*st .. 64*st+63): lanes 0-31 take 16-byte chunks
+  // {4st, 4st+1}, lanes 32-63 take {4st+2, 4st+3} of their row.
+#define MOE_F8_READ(st_)                                                                            \
+  do {                                                                                              \
+    const int c0_ = ((4 * (st_) + 2 * hi) ^ sw) * 16, c1_ = ((4 * (st_) + 2 * hi + 1) ^ sw) * 16;  \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                                \
+      const char* r_ = sb_ + (bblock(j) * 32 + lr) * ROW;                                           \
+      b[st_][j][0] = *(const u32x4*)(r_ + c0_);                                                     \
+      b[st_][j][1] = *(const u32x4*)(r_ + c1_);                                                     \
+    }                                                                                               \
+    _Pragma("unroll") for (int i = 0; i < NL; ++i) {                                                \
+      const char* r_ = sa_ + ((wm + 2 * i) * 32 + lr) * ROW;                                        \
+      a[st_][i][0] = *(const u32x4*)(r_ + c0_);                                                     \
+      a[st_][i][1] = *(const u32x4*)(r_ + c1_);                                                     \
+    }                                                                                               \
+  } while (0)
+
+// One K step: every LDS read of the step (both sub-steps' fragments and the
+// activation scales) first, so none of them follows a ring DMA in program order;
+// then A's ring DMAs with the first sub-step's MFMAs, B's with the second's and
+// the scaled fold of the partials.
+#define MOE_F8_KLOOP                                                                                 \
+  for (int kt = 0; kt < nk; ++kt) {                                                                  \
+    wait_vm_barrier<VMN>();                                                                          \
+    const char* sa_ = lds + (kt % SA) * ASLOT;                                                       \
+    const char* sb_ = lds + SA * ASLOT + (kt % SB) * BSLOT;                                          \
+    float sbk[TN];                                                                                   \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j) sbk[j] = sbn[j];                                  \
+    {                                                                                                \
+      const int kn_ = kt + 1 < nk ? kt + 1 : kt;                                                     \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j) sbn[j] = SBg[(int64_t)sbrow[j] * nkb + kn_];    \
+    }                                                                                                \
+    u32x4 a[2][NL][2], b[2][TN][2];                                                                  \
+    MOE_F8_READ(0);                                                                                  \
+    MOE_F8_READ(1);                                                                                  \
+    /* this step's activation scales: rows 8*(e/4) + 4*hi + (e%4) of each block */                  \
+    float sa[NL][16];                                                                                \
+    _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                   \
+      _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                                \
+        const int r_ = (wm + 2 * i) * 32 + 8 * q + 4 * hi;                                           \
+        /* read as u32x4 like the fragments (no wait on the ring DMAs in flight) */                \
+        const u32x4 u_ = *(const u32x4*)(sa_ + ADATA + ((r_ / RW) * 64 + r_ % RW) * 4);             \
+        const float4 v_ = __builtin_bit_cast(float4, u_);                                            \
+        sa[i][4 * q + 0] = v_.x; sa[i][4 * q + 1] = v_.y; sa[i][4 * q + 2] = v_.z; sa[i][4 * q + 3] = v_.w; \
+      }                                                                                              \
+    __builtin_amdgcn_sched_barrier(0);                                                               \
+    MOE_F8_ISSUE_A(kt + SA - 1, 0, AI, true);                                                        \
+    f32x16 part[NL][TN];                                                                             \
+    _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                   \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                               \
+        f32x16 z_;                                                                                   \
+        _Pragma("unroll") for (int e = 0; e < 16; ++e) z_[e] = 0.0f;                                 \
+        part[i][j] = mma_fp8(a[0][i][0], a[0][i][1], b[0][j][0], b[0][j][1], z_);                    \
+      }                                                                                              \
+    sub_schedule<0, NL * TN, 0, AL>();                                                               \
+    __builtin_amdgcn_sched_barrier(0);                                                               \
+    MOE_F8_ISSUE_B(kt + SB - 1, 0, BI);                                                              \
+    _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                   \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                 \
+        part[i][j] = mma_fp8(a[1][i][0], a[1][i][1], b[1][j][0], b[1][j][1], part[i][j]);            \
+    sub_schedule<0, NL * TN, 0, BI>();                                                               \
+    _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                   \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                 \
+        _Pragma("unroll") for (int e = 0; e < 16; ++e)                                               \
+          acc[i][j][e] += part[i][j][e] * (sa[i][e] * sbk[j]);                                       \
+  }
+
+  if (tm_live <= 1) {
+    constexpr int NL = 1;
+    MOE_F8_KLOOP
+  } else {
+    constexpr int NL = TM;
+    MOE_F8_KLOOP
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#undef MOE_F8_KLOOP
+#undef MOE_F8_READ
+#undef MOE_F8_ISSUE_A
+#undef MOE_F8_ISSUE_B
+
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    if (i >= tm_live) continue;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = (wm + 2 * i) * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+      if (row >= rows) continue;
+      const int prow = r0 + row;
+      if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int j = 0; j < TN / 2; ++j) {
+          const int col = nt * (BN / 2) + (wn * (TN / 2) + j) * 32 + lr;
+          if (col < p.N)
+            ((uint16_t*)p.C)[(int64_t)prow * p.N + col] =
+                (uint16_t)f32_to_bf16_bits(silu_mul8(acc[i][j][e], acc[i][j + TN / 2][e]));
+        }
+      } else if constexpr (EPI == EPI_SCATTER) {
+        const int tok = p.c_rows ? p.c_rows[prow] : prow;
+        const float w = p.row_w[prow];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = nt * BN + bblock(j) * 32 + lr;
+          if (col < p.N) atomicAdd((float*)p.C + (int64_t)tok * p.N + col, w * acc[i][j][e]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = nt * BN + bblock(j) * 32 + lr;
+          if (col < p.N) ((uint16_t*)p.C)[(int64_t)prow * p.N + col] = (uint16_t)f32_to_bf16_bits(acc[i][j][e]);
+        }
+      }
+    }
+  }
+}
+
+template <int TM, int TN, int SA, int SB, int EPI>
+static hipError_t launch8_split(const GemmFp8Params& p, int grid_m, hipStream_t s) {
+  constexpr int BM = 2 * TM * 32, BN = 2 * TN * 32;
+  constexpr int lds_bytes = SA * (BM * 128 + 1024) + SB * BN * 128;
+  static_assert(lds_bytes <= 160 * 1024, "LDS");
+  auto kern = gemm_fp8_split_kernel<TM, TN, SA, SB, EPI>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t grid = (int64_t)grid_m * p.ntn;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds_bytes, s, p);
+  return hipGetLastError();
+}
+
+#ifndef MOE_TILE_FP8
+#define MOE_TILE_FP8 -1
+#endif
+
+// kind 0: register-staged 128 x 128 (any size); kind 1: pipelined 128 x 256
+// (A and B buffers addressed with 31-bit offsets)
+GemmShape gemm_fp8_shape(int rows_hint, int64_t a_bytes, int64_t b_bytes) {
   GemmShape g;
   (void)rows_hint;
-  g.bm = 128; g.bn = 128; g.kind = 0;
+  const bool pipe_ok = a_bytes < (1LL << 31) && b_bytes < (1LL << 31);
+  g.kind = pipe_ok ? 1 : 0;
+  if (MOE_TILE_FP8 >= 0 && pipe_ok) g.kind = MOE_TILE_FP8;
+  g.bm = 128;
+  g.bn = g.kind == 0 ? 128 : 256;
   return g;
 }
 
@@ -258,7 +571,14 @@ static hipError_t launch8(const GemmFp8Params& p, int grid_m, hipStream_t s) {
 }
 
 hipError_t launch_gemm_fp8(int epi, const GemmFp8Params& p, const GemmShape& g, int grid_m, hipStream_t s) {
-  (void)g;
+  if (g.kind == 1) {
+    switch (epi) {
+      case EPI_SWIGLU: return launch8_split<2, 4, 3, 3, EPI_SWIGLU>(p, grid_m, s);
+      case EPI_SCATTER: return launch8_split<2, 4, 3, 3, EPI_SCATTER>(p, grid_m, s);
+      case EPI_STORE: return launch8_split<2, 4, 3, 3, EPI_STORE>(p, grid_m, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (epi) {
     case EPI_SWIGLU: return launch8<2, 2, 2, 2, EPI_SWIGLU>(p, grid_m, s);
     case EPI_SCATTER: return launch8<2, 2, 2, 2, EPI_SCATTER>(p, grid_m, s);

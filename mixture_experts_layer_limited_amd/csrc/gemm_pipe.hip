@@ -20,40 +20,9 @@
 // activations is never written.
 #include "common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace moe {
-
-typedef __attribute__((address_space(3))) char lds_char;
-
-// 16 bytes per lane from a buffer straight into LDS at dst + 16 * lane.  Kept
-// out of the kernel templates: the host pass drops a kernel template whose body
-// names this builtin.
-__device__ __attribute__((always_inline)) inline void dma16(__amdgpu_buffer_rsrc_t r, lds_char* dst, uint32_t voff,
-                                                            uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int n = bytes >= 0x7fffffffLL ? 0x7fffffff : (int)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
-}
-
-// Wait until at most n vector-memory operations of this wave are in flight,
-// then meet the other waves at the barrier.  The asm block is also a compiler
-// barrier for memory operations.
-template <int N>
-__device__ __forceinline__ void wait_vm_barrier() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
-// XOR swizzle of the 16-byte chunk index of row r: conflict-free 128-bit reads
-// of 8 and of 16 consecutive rows at one logical chunk.
-template <int ROW>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (ROW == 64) return ((r >> 1) ^ (r >> 3)) & 3;
-  else return (r & 7) ^ ((r >> 3) & 1);
-}
 
 template <int Q, int M, int LI>
 __device__ __forceinline__ void pipe_schedule_mfmas() {
@@ -269,6 +238,255 @@ __global__ __launch_bounds__(256, OCC) void gemm_pipe_kernel(GemmParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Split-ring kernel for the large prefill GEMMs.  A and B tiles have rings of
+// their own (depth SA <= SB slots of 64 bf16 of K), so the weight stream (B,
+// mostly HBM misses) runs further ahead than the activation rows (A, mostly L2
+// hits shared by every n-tile of the m-tile).  Within a K step the fragment
+// reads of sub-step st+1 are issued among the MFMAs of sub-step st, so only the
+// first sub-step's LDS latency is exposed per step.
+//
+// DMA issue order per step: A(kt + SA - 1), then B(kt + SB - 1); the wait at the
+// top of step kt leaves exactly the instructions issued after the last one that
+// step kt needs in flight (VMN).
+
+template <int TM, int TN, int SA, int SB, int EPI, int ODT>
+__global__ __launch_bounds__(256, 1) void gemm_split_kernel(GemmParams p) {
+  constexpr int WM = 2, WN = 2, NW = 4;
+  constexpr int BM = WM * TM * 32;
+  constexpr int BN = WN * TN * 32;
+  constexpr int ROW = 128, CPR = 8, RPI = 8, NSUB = 4;  // NSUB is fixed: the K loop names sub-steps 0..3
+  constexpr int ASLOT = BM * ROW, BSLOT = BN * ROW;
+  constexpr int AI = BM / RPI / NW, BI = BN / RPI / NW;
+  constexpr int LI = AI + BI;
+  // A(kt) is issued SA-1 steps before step kt; with SB > SA, B(kt) went out even
+  // earlier and only B of A(kt)'s step follows it, else B(kt) is that step's last.
+  constexpr int VMN = SB > SA ? BI + (SA - 2) * LI : (SA - 2) * LI;
+  static_assert(AI * RPI * NW == BM && BI * RPI * NW == BN, "tile / wave mismatch");
+  static_assert(SA >= 2 && SB >= SA && VMN < 64, "ring depths");
+  static_assert(EPI != EPI_SWIGLU || TN % 2 == 0, "SwiGLU pairs gate and up tiles");
+
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  lds_char* const lds3 = (lds_char*)lds;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+
+  const int total = p.tiles ? *p.n_mtiles_dev : p.n_mtiles * p.ntn;
+  const int P = blockIdx.x;
+  if (P >= total) return;
+  const int L = xcd_remap(P, total);
+  int grp, r0, r1, nt;
+  if (p.tiles) {
+    const int4 t = p.tiles[L];
+    grp = t.x; r0 = t.y; r1 = t.z; nt = t.w;
+  } else {
+    const int mt = L / p.ntn;
+    nt = L - mt * p.ntn;
+    grp = 0; r0 = mt * BM; r1 = min(p.M, r0 + BM);
+  }
+  const int rows = r1 - r0;
+  const int64_t krow = (int64_t)p.K * 2;
+  const char* Bg = (const char*)p.B + (int64_t)grp * p.b_gstride * 2;
+  const int b_nrows = (EPI == EPI_SWIGLU) ? 2 * p.N : p.N;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, p.a_nrows * krow);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bg, (int64_t)b_nrows * krow);
+
+  const int lrow = lane / CPR, lslot = lane % CPR;
+  uint32_t voa[AI], vob[BI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int r = (wave * AI + i) * RPI + lrow;
+    const int chunk = lslot ^ swz<ROW>(r);
+    if (r < rows) {
+      const int src = p.a_rows ? p.a_rows[r0 + r] : r0 + r;
+      voa[i] = (uint32_t)((int64_t)src * krow + chunk * 16);
+    } else {
+      voa[i] = 0x40000000u;  // past the tile: out of range (zero fill, no traffic) or harmless
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const int r = (wave * BI + i) * RPI + lrow;
+    const int chunk = lslot ^ swz<ROW>(r);
+    int wrow;
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int j = min(nt * (BN / 2) + (r % (BN / 2)), p.N - 1);
+      wrow = (r < BN / 2) ? j : p.N + j;
+    } else {
+      wrow = min(nt * BN + r, p.N - 1);
+    }
+    vob[i] = (uint32_t)((int64_t)wrow * krow + chunk * 16);
+  }
+
+  const int nk = p.K * 2 / ROW;
+  lds_char* const ring_a = lds3;
+  lds_char* const ring_b = lds3 + SA * ASLOT;
+
+  // DMA instructions [lo, hi) of step kt_'s A (or B) slot; the tail steps read
+  // out of range (zero fill, no traffic) so the vmcnt bookkeeping stays fixed.
+#define MOE_SPLIT_ISSUE_A(kt_, lo_, hi_)                                               \
+  do {                                                                                 \
+    lds_char* slot_ = ring_a + ((kt_) % SA) * ASLOT;                                   \
+    const uint32_t soff_ = (kt_) < nk ? (uint32_t)(kt_) * ROW : 0x80000000u;           \
+    _Pragma("unroll") for (int i = (lo_); i < (hi_); ++i)                              \
+      dma16(ra, slot_ + (wave * AI + i) * 1024, voa[i], soff_);                        \
+  } while (0)
+#define MOE_SPLIT_ISSUE_B(kt_, lo_, hi_)                                               \
+  do {                                                                                 \
+    lds_char* slot_ = ring_b + ((kt_) % SB) * BSLOT;                                   \
+    const uint32_t soff_ = (kt_) < nk ? (uint32_t)(kt_) * ROW : 0x80000000u;           \
+    _Pragma("unroll") for (int i = (lo_); i < (hi_); ++i)                              \
+      dma16(rb, slot_ + (wave * BI + i) * 1024, vob[i], soff_);                        \
+  } while (0)
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  int tm_live = 0;  // row blocks wm, wm+2, ... holding live rows form a prefix
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+    if ((wm + 2 * i) * 32 < rows) tm_live = i + 1;
+  tm_live = __builtin_amdgcn_readfirstlane(tm_live);
+
+  auto bblock = [&](int tn) {
+    if constexpr (EPI == EPI_SWIGLU)
+      return tn < TN / 2 ? wn * (TN / 2) + tn : WN * (TN / 2) + wn * (TN / 2) + (tn - TN / 2);
+    else
+      return wn * TN + tn;
+  };
+
+  const int lr = lane & 31, hi = lane >> 5;
+  const int sw = swz<ROW>(lr);
+
+  // Prologue: the issues of virtual steps 1-SB .. -1.
+#pragma unroll
+  for (int v = 1 - SB; v < 0; ++v) {
+    if (v + SA - 1 >= 0) MOE_SPLIT_ISSUE_A(v + SA - 1, 0, AI);
+    if (v + SB - 1 >= 0) MOE_SPLIT_ISSUE_B(v + SB - 1, 0, BI);
+  }
+
+#define MOE_SPLIT_READ(buf_, st_)                                                                   \
+  do {                                                                                              \
+    const int coff_ = ((2 * (st_) + hi) ^ sw) * 16;                                                 \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                  \
+      b[buf_][j] = *(const u32x4*)(sb_ + (bblock(j) * 32 + lr) * ROW + coff_);                      \
+    _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                  \
+      a[buf_][i] = *(const u32x4*)(sa_ + ((wm + 2 * i) * 32 + lr) * ROW + coff_);                   \
+  } while (0)
+
+// Sub-step ST issues the reads of sub-step ST+1, its share of the step's ring
+// DMAs (A's in the first half of the step, B's in the second, keeping the issue
+// order the vmcnt bound assumes) and its MFMAs; a scheduling fence closes it.
+#define MOE_SPLIT_SUB(ST)                                                                            \
+  do {                                                                                               \
+    constexpr int nxt_ = (ST) + 1 < NSUB ? NL + TN : 0;                                              \
+    constexpr int h_ = NSUB / 2;                                                                     \
+    if constexpr ((ST) + 1 < NSUB) MOE_SPLIT_READ(((ST) + 1) & 1, (ST) + 1);                         \
+    if constexpr ((ST) < h_) MOE_SPLIT_ISSUE_A(kt + SA - 1, (ST) * AI / h_, ((ST) + 1) * AI / h_);   \
+    else MOE_SPLIT_ISSUE_B(kt + SB - 1, ((ST) - h_) * BI / h_, ((ST) - h_ + 1) * BI / h_);           \
+    _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                   \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                 \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[(ST) & 1][i]), \
+                                                            __builtin_bit_cast(bf16x8, b[(ST) & 1][j]), \
+                                                            acc[i][j], 0, 0, 0);                     \
+    sub_schedule<0, NL * TN, nxt_, ((ST) < h_ ? AI : BI) / h_>();                                    \
+    __builtin_amdgcn_sched_barrier(0);                                                               \
+  } while (0)
+
+#define MOE_SPLIT_KLOOP                                                                              \
+  for (int kt = 0; kt < nk; ++kt) {                                                                  \
+    wait_vm_barrier<VMN>();                                                                          \
+    const char* sa_ = lds + (kt % SA) * ASLOT;                                                       \
+    const char* sb_ = lds + SA * ASLOT + (kt % SB) * BSLOT;                                          \
+    u32x4 a[2][NL], b[2][TN];                                                                        \
+    MOE_SPLIT_READ(0, 0);                                                                            \
+    __builtin_amdgcn_sched_barrier(0);                                                               \
+    MOE_SPLIT_SUB(0);                                                                                \
+    MOE_SPLIT_SUB(1);                                                                                \
+    MOE_SPLIT_SUB(2);                                                                                \
+    MOE_SPLIT_SUB(3);                                                                                \
+  }
+
+  if (tm_live <= 1) {
+    constexpr int NL = 1;
+    MOE_SPLIT_KLOOP
+  } else if (TM > 2 && tm_live == 2) {
+    constexpr int NL = TM > 2 ? 2 : TM;
+    MOE_SPLIT_KLOOP
+  } else if (TM > 3 && tm_live == 3) {
+    constexpr int NL = TM > 3 ? 3 : TM;
+    MOE_SPLIT_KLOOP
+  } else {
+    constexpr int NL = TM;
+    MOE_SPLIT_KLOOP
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#undef MOE_SPLIT_KLOOP
+#undef MOE_SPLIT_SUB
+#undef MOE_SPLIT_READ
+#undef MOE_SPLIT_ISSUE_A
+#undef MOE_SPLIT_ISSUE_B
+
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    if (i >= tm_live) continue;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = (wm + 2 * i) * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+      if (row >= rows) continue;
+      const int prow = r0 + row;
+      if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int j = 0; j < TN / 2; ++j) {
+          const int col = nt * (BN / 2) + (wn * (TN / 2) + j) * 32 + lr;
+          if (col < p.N)
+            Elem<ODT>::store((typename Elem<ODT>::T*)p.C, (int64_t)prow * p.N + col,
+                             silu_mul_p(acc[i][j][e], acc[i][j + TN / 2][e]));
+        }
+      } else if constexpr (EPI == EPI_SCATTER) {
+        const int tok = p.c_rows ? p.c_rows[prow] : prow;
+        const float w = p.row_w[prow];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = nt * BN + bblock(j) * 32 + lr;
+          if (col < p.N) atomicAdd((float*)p.C + (int64_t)tok * p.N + col, w * acc[i][j][e]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = nt * BN + bblock(j) * 32 + lr;
+          if (col < p.N) Elem<ODT>::store((typename Elem<ODT>::T*)p.C, (int64_t)prow * p.N + col, acc[i][j][e]);
+        }
+      }
+    }
+  }
+}
+
+template <int TM, int TN, int SA, int SB, int EPI, int ODT>
+static hipError_t launch_split(const GemmParams& p, int grid_m, hipStream_t s) {
+  constexpr int BM = 2 * TM * 32, BN = 2 * TN * 32;
+  constexpr int lds_bytes = (SA * BM + SB * BN) * 128;
+  static_assert(lds_bytes <= 160 * 1024, "LDS");
+  auto kern = gemm_split_kernel<TM, TN, SA, SB, EPI, ODT>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t grid = (int64_t)grid_m * p.ntn;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds_bytes, s, p);
+  return hipGetLastError();
+}
+
 template <int TM, int TN, int S, int OCC, int ROWB, int EPI, int ODT>
 static hipError_t launch_pipe(const GemmParams& p, int grid_m, hipStream_t s) {
   constexpr int BM = 2 * TM * 32, BN = 2 * TN * 32;
@@ -292,6 +510,8 @@ static hipError_t launch_pipe(const GemmParams& p, int grid_m, hipStream_t s) {
 // kind 12: 128 x 256, 128-byte rows, 3-slot ring
 // kind 13: 128 x 256, 64-byte rows, 6-slot ring
 // kind 14:  64 x 256, 128-byte rows, 4-slot ring
+// kind 15: 256 x 256 split rings, A 2 slots + B 3 slots (160 KB)
+// kind 16: 128 x 256 split rings, A 3 slots + B 3 slots
 template <int EPI, int ODT>
 static hipError_t pipe_kind(const GemmParams& p, const GemmShape& g, int grid_m, hipStream_t s) {
   switch (g.kind) {
@@ -299,6 +519,8 @@ static hipError_t pipe_kind(const GemmParams& p, const GemmShape& g, int grid_m,
     case 12: return launch_pipe<2, 4, 3, 1, 128, EPI, ODT>(p, grid_m, s);
     case 13: return launch_pipe<2, 4, 6, 1, 64, EPI, ODT>(p, grid_m, s);
     case 14: return launch_pipe<1, 4, 4, 1, 128, EPI, ODT>(p, grid_m, s);
+    case 15: return launch_split<4, 4, 2, 3, EPI, ODT>(p, grid_m, s);
+    case 16: return launch_split<2, 4, 3, 3, EPI, ODT>(p, grid_m, s);
     default: return launch_pipe<4, 4, 4, 1, 64, EPI, ODT>(p, grid_m, s);
   }
 }

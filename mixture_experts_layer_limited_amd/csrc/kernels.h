@@ -62,8 +62,9 @@ struct GemmFp8Params {
   int n_mtiles;
   int M;
   int ntn;
+  int64_t a_nrows;        // rows of A and of its scales (bounds of the activation buffers)
 };
-GemmShape gemm_fp8_shape(int rows_hint);
+GemmShape gemm_fp8_shape(int rows_hint, int64_t a_bytes, int64_t b_bytes);
 hipError_t launch_gemm_fp8(int epi, const GemmFp8Params& p, const GemmShape& g, int grid_m, hipStream_t s);
 
 struct RouteParams {

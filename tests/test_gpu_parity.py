@@ -196,6 +196,8 @@ SMALL = {
     "v2_lite_small": _reduced("v2_lite_bf16", tokens=203),
     "v3_small": _reduced("v3_prefill_bf16", tokens=300, hidden=1024, inter=256, n_experts=64, shared_inter=256),
     "v3_small_t1": _reduced("v3_prefill_bf16", tokens=1, hidden=1024, inter=256, n_experts=64, shared_inter=256),
+    # about 300 rows per expert: the 256-row tiles, two ragged m-tiles per expert
+    "v3_mid": _reduced("v3_prefill_bf16", tokens=1203, hidden=512, inter=384, n_experts=32, shared_inter=128),
     "fp8_small": _reduced("v3_fp8", tokens=300, hidden=1024, inter=256, n_experts=64, shared_inter=256),
     "fp8_small_ragged": _reduced("v3_fp8", tokens=45, hidden=512, inter=384, n_experts=64, shared_inter=128),
 }
