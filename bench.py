@@ -15,6 +15,7 @@ stream; `grouped_gemm` covers both routed GEMMs (gate/up and down);
 """
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -28,6 +29,36 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "MoE layer tokens/s + grouped-GEMM TFLOPS (% MFMA peak) at V3 shape, 1 GPU"
 
 
+def csrc_sha256():
+    """Hash of the kernel sources: counter figures taken on other sources are stale."""
+    d = os.path.join(ROOT, "mixture_experts_layer_limited_amd", "csrc")
+    h = hashlib.sha256()
+    for fn in sorted(os.listdir(d)):
+        if fn.endswith((".hip", ".h", ".cpp")):
+            h.update(fn.encode())
+            with open(os.path.join(d, fn), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(config):
+    """HBM bytes per launch of the routed gate/up GEMM from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary of this workload (calibrated
+    against a plain copy), or None when there is none or the kernels changed."""
+    path = os.path.join(ROOT, "profiles", f"gemm_traffic_{config}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            k, sep, v = line.partition(":")
+            if sep and k.strip() and " " not in k.strip():
+                fields[k.strip()] = v.strip()
+    if fields.get("csrc_sha256") != csrc_sha256() or "routed_gate_up_traffic_bytes" not in fields:
+        return None
+    return float(fields["routed_gate_up_traffic_bytes"])
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -35,7 +66,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="v3_prefill_bf16")
     p.add_argument("--epilogue", choices=["store", "scatter"], default="store")
-    p.add_argument("--cpu-sample", type=int, default=8, help="tokens in the oracle's timed sample (0 = skip)")
+    p.add_argument("--cpu-sample", type=int, default=40, help="tokens in the oracle's timed sample (0 = skip)")
     return p.parse_args()
 
 
@@ -190,7 +221,8 @@ def main():
     else:
         achieved = flops1 / (g1 * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak}
-    roof.update({"traffic": None, "kernel": "routed gate/up grouped GEMM + SiLU*up (gemm_kernel, EPI_SWIGLU)",
+    roof.update({"traffic": measured_traffic(cfg.name),
+                 "kernel": "routed gate/up grouped GEMM with the SiLU*up epilogue",
                  "ms": g1, "algorithmic_bytes": bytes1, "algorithmic_flops": flops1})
     gg_tflops = (flops1 + flops2) / ((g1 + g2) * 1e-3) / 1e12
     result = {
