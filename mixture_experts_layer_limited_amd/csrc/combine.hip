@@ -95,33 +95,55 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
-// One wavefront per (row, 128-column tile), two values per lane:
+// Activation quantisation, one 1x128 tile per 16 lanes:
 // scale = fp32(amax / 448) (1 if amax == 0), code = E4M3(fp32(v / scale)).
 template <int IDT>
 __global__ __launch_bounds__(256) void quantize_kernel(int64_t rows, int64_t cols, const void* __restrict__ in,
                                                        uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  // 16 lanes per 1x128 tile, 8 consecutive values per lane: one 16-byte (bf16)
+  // or two (fp32) loads and one 8-byte store of codes per lane.
   using T = typename Elem<IDT>::T;
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63, sub = lane & 15;
   const int64_t tiles_per_row = cols / 128;
-  const int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t tile = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   if (tile >= rows * tiles_per_row) return;
   const int64_t r = tile / tiles_per_row, c0 = (tile % tiles_per_row) * 128;
-  const int64_t base = r * cols + c0 + 2 * lane;
-  const float v0 = Elem<IDT>::load((const T*)in, base);
-  const float v1 = Elem<IDT>::load((const T*)in, base + 1);
-  const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
-  const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
-  const uint32_t q0 = f32_to_e4m3(v0 / scale);
-  const uint32_t q1 = f32_to_e4m3(v1 / scale);
-  *(uint16_t*)(codes + base) = (uint16_t)(q0 | (q1 << 8));
-  if (lane == 0) scales[r * tiles_per_row + c0 / 128] = scale;
+  const int64_t base = r * cols + c0 + 8 * sub;
+  float v[8];
+  if constexpr (IDT == MOE_DT_BF16) {
+    const u32x4 w = *(const u32x4*)((const T*)in + base);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = __uint_as_float(w[q] << 16);
+      v[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+    }
+  } else {
+    const float4 w0 = *(const float4*)((const float*)in + base);
+    const float4 w1 = *(const float4*)((const float*)in + base + 4);
+    v[0] = w0.x; v[1] = w0.y; v[2] = w0.z; v[3] = w0.w;
+    v[4] = w1.x; v[5] = w1.y; v[6] = w1.z; v[7] = w1.w;
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(v[q]));
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  const float scale = m > 0.0f ? m / 448.0f : 1.0f;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    lo |= f32_to_e4m3(v[q] / scale) << (8 * q);
+    hi |= f32_to_e4m3(v[q + 4] / scale) << (8 * q);
+  }
+  *(uint2*)(codes + base) = make_uint2(lo, hi);
+  if (sub == 0) scales[r * tiles_per_row + c0 / 128] = scale;
 }
 
 hipError_t launch_quantize(int in_dt, int64_t rows, int64_t cols, const void* in, uint8_t* codes, float* scales,
                            hipStream_t s) {
   const int64_t tiles = rows * (cols / 128);
   if (tiles <= 0) return hipSuccess;
-  const int64_t grid = (tiles + 3) / 4;
+  const int64_t grid = (tiles + 15) / 16;
   if (in_dt == MOE_DT_BF16)
     hipLaunchKernelGGL(quantize_kernel<MOE_DT_BF16>, dim3((unsigned)grid), dim3(256), 0, s, rows, cols, in, codes,
                        scales);

@@ -1,23 +1,29 @@
-// Pipelined grouped bf16 GEMM for the large expert GEMMs (gate/up with the
-// SiLU*up epilogue, down with the row-store or weighted scatter-add epilogue).
+// Pipelined grouped bf16 GEMMs for the expert FFNs (gate/up with the SiLU*up
+// epilogue, down with the row-store or weighted scatter-add epilogue), after the
+// grouped-GEMM step of the MoE inference walkthrough (zhiyuanblog.org/blog/
+// moe-inference, §3.3):
 //
-// C[p, n] = sum_k A[src(p), k] * B[g][n, k] over the rows p of m-tile (g, r0, r1)
+//   C[p, n] = sum_k A[src(p), k] * B[g][n, k] over the rows p of m-tile (g, r0, r1)
 //
-// Each K step stages BK = 32 bf16 (64 bytes) of every A row and every B row in
-// one slot of an S-slot LDS ring.  Slots are filled straight from memory by
-// buffer_load ... lds (no register staging), S-1 steps ahead of the MFMAs, so
-// several steps of weight traffic are in flight per CU while the matrix cores
-// work; an explicit "s_waitcnt vmcnt(n); s_barrier" per step releases exactly
-// the slot that is about to be read.  A 16-byte chunk c of row r sits at chunk
-// c ^ (((r >> 1) ^ (r >> 3)) & 3) of its 64-byte LDS row, which keeps the 128-bit
-// fragment reads of 8 (and of 16) consecutive rows on distinct banks.
+// Operand tiles stream straight from memory into LDS rings with buffer_load ...
+// lds (no register staging), several K steps ahead of the MFMAs; an explicit
+// "s_waitcnt vmcnt(n); s_barrier" per step releases exactly the slot about to be
+// read.  Rows are gathered through permuted_src by per-lane buffer offsets, so
+// the permuted copy of the activations is never written; rows past a tile and
+// the K tail read out of the buffer's range, which fills zeros without traffic.
+// 16-byte chunks are XOR-swizzled within each LDS row so the 128-bit fragment
+// reads of 8 and of 16 consecutive rows hit distinct banks.
 //
-// Work-group: 2 x 2 waves, each owning TM row blocks and TN column blocks of
-// 32 (v_mfma_f32_32x32x16_bf16).  Wave row wm takes row blocks wm, wm+2, ...
-// so the two wave rows stay balanced when the tile has fewer live rows than
-// BM; row blocks without live rows issue no MFMAs.  Rows are gathered through
-// permuted_src by the per-lane buffer offsets, so the permuted copy of the
-// activations is never written.
+// gemm_pipe_kernel: one ring holding A and B (64- or 128-byte K rows), 2 x 2
+//   waves; used for decode-sized groups (64 x 256 tiles).
+// gemm_split_kernel: separate A and B rings of 128-byte K rows (B runs deeper),
+//   k16 sub-steps whose fragment reads overlap the previous sub-step's MFMAs,
+//   and an LDS-staged bf16 epilogue with 16-byte row stores; 256 x 256 tiles
+//   for prefill-sized groups.
+// In both, wave row wm takes row blocks wm, wm+WM, ... so the wave rows stay
+// balanced when a tile has fewer live rows than BM; row blocks without live rows
+// issue no MFMAs (the live blocks of a wave are a prefix, so the K loop is
+// specialised on their count and stays branch-free).
 #include "common.h"
 #include "kernels.h"
 #include "lds_dma.h"
@@ -250,9 +256,9 @@ __global__ __launch_bounds__(256, OCC) void gemm_pipe_kernel(GemmParams p) {
 // top of step kt leaves exactly the instructions issued after the last one that
 // step kt needs in flight (VMN).
 
-template <int TM, int TN, int SA, int SB, int EPI, int ODT>
-__global__ __launch_bounds__(256, 1) void gemm_split_kernel(GemmParams p) {
-  constexpr int WM = 2, WN = 2, NW = 4;
+template <int WM, int WN, int TM, int TN, int SA, int SB, int EPI, int ODT>
+__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_split_kernel(GemmParams p) {
+  constexpr int NW = WM * WN;
   constexpr int BM = WM * TM * 32;
   constexpr int BN = WN * TN * 32;
   constexpr int ROW = 128, CPR = 8, RPI = 8, NSUB = 4;  // NSUB is fixed: the K loop names sub-steps 0..3
@@ -352,7 +358,7 @@ __global__ __launch_bounds__(256, 1) void gemm_split_kernel(GemmParams p) {
   int tm_live = 0;  // row blocks wm, wm+2, ... holding live rows form a prefix
 #pragma unroll
   for (int i = 0; i < TM; ++i)
-    if ((wm + 2 * i) * 32 < rows) tm_live = i + 1;
+    if ((wm + WM * i) * 32 < rows) tm_live = i + 1;
   tm_live = __builtin_amdgcn_readfirstlane(tm_live);
 
   auto bblock = [&](int tn) {
@@ -378,7 +384,7 @@ __global__ __launch_bounds__(256, 1) void gemm_split_kernel(GemmParams p) {
     _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                  \
       b[buf_][j] = *(const u32x4*)(sb_ + (bblock(j) * 32 + lr) * ROW + coff_);                      \
     _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                  \
-      a[buf_][i] = *(const u32x4*)(sa_ + ((wm + 2 * i) * 32 + lr) * ROW + coff_);                   \
+      a[buf_][i] = *(const u32x4*)(sa_ + ((wm + WM * i) * 32 + lr) * ROW + coff_);                   \
   } while (0)
 
 // Sub-step ST issues the reads of sub-step ST+1, its share of the step's ring
@@ -434,12 +440,54 @@ __global__ __launch_bounds__(256, 1) void gemm_split_kernel(GemmParams p) {
 #undef MOE_SPLIT_ISSUE_A
 #undef MOE_SPLIT_ISSUE_B
 
+  if constexpr (ODT == MOE_DT_BF16 && (EPI == EPI_STORE || EPI == EPI_SWIGLU)) {
+    // bf16 tile through LDS (the ring is idle now): 2-byte writes in MFMA layout,
+    // then 16-byte row-contiguous global stores.  Rows are padded by 16 bytes so
+    // the two half-waves (rows 4 apart) write disjoint banks.
+    constexpr int OC = EPI == EPI_SWIGLU ? BN / 2 : BN;  // output columns of the tile
+    constexpr int RB = OC * 2 + 16;                      // LDS bytes per staged row
+    static_assert(BM * RB <= SA * ASLOT + SB * BSLOT, "staging fits the ring");
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if (i >= tm_live) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = (wm + WM * i) * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+        char* rp = lds + row * RB;
+        if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+          for (int j = 0; j < TN / 2; ++j) {
+            const int c = (wn * (TN / 2) + j) * 32 + lr;
+            *(uint16_t*)(rp + 2 * c) = (uint16_t)f32_to_bf16_bits(silu_mul_p(acc[i][j][e], acc[i][j + TN / 2][e]));
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int c = bblock(j) * 32 + lr;
+            *(uint16_t*)(rp + 2 * c) = (uint16_t)f32_to_bf16_bits(acc[i][j][e]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int CPRo = OC / 8;  // 16-byte chunks per output row
+    const int c0 = nt * OC;
+    for (int q = tid; q < BM * CPRo; q += NW * 64) {
+      const int row = q / CPRo, ch = q % CPRo;
+      const int col = c0 + ch * 8;
+      if (row < rows && col < p.N)
+        *(u32x4*)((uint16_t*)p.C + (int64_t)(r0 + row) * p.N + col) = *(const u32x4*)(lds + row * RB + ch * 16);
+    }
+    return;
+  }
+
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     if (i >= tm_live) continue;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int row = (wm + 2 * i) * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+      const int row = (wm + WM * i) * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
       if (row >= rows) continue;
       const int prow = r0 + row;
       if constexpr (EPI == EPI_SWIGLU) {
@@ -469,12 +517,12 @@ __global__ __launch_bounds__(256, 1) void gemm_split_kernel(GemmParams p) {
   }
 }
 
-template <int TM, int TN, int SA, int SB, int EPI, int ODT>
+template <int WM, int WN, int TM, int TN, int SA, int SB, int EPI, int ODT>
 static hipError_t launch_split(const GemmParams& p, int grid_m, hipStream_t s) {
-  constexpr int BM = 2 * TM * 32, BN = 2 * TN * 32;
+  constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   constexpr int lds_bytes = (SA * BM + SB * BN) * 128;
   static_assert(lds_bytes <= 160 * 1024, "LDS");
-  auto kern = gemm_split_kernel<TM, TN, SA, SB, EPI, ODT>;
+  auto kern = gemm_split_kernel<WM, WN, TM, TN, SA, SB, EPI, ODT>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
@@ -483,7 +531,7 @@ static hipError_t launch_split(const GemmParams& p, int grid_m, hipStream_t s) {
   }
   const int64_t grid = (int64_t)grid_m * p.ntn;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds_bytes, s, p);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WM * WN * 64), lds_bytes, s, p);
   return hipGetLastError();
 }
 
@@ -519,8 +567,8 @@ static hipError_t pipe_kind(const GemmParams& p, const GemmShape& g, int grid_m,
     case 12: return launch_pipe<2, 4, 3, 1, 128, EPI, ODT>(p, grid_m, s);
     case 13: return launch_pipe<2, 4, 6, 1, 64, EPI, ODT>(p, grid_m, s);
     case 14: return launch_pipe<1, 4, 4, 1, 128, EPI, ODT>(p, grid_m, s);
-    case 15: return launch_split<4, 4, 2, 3, EPI, ODT>(p, grid_m, s);
-    case 16: return launch_split<2, 4, 3, 3, EPI, ODT>(p, grid_m, s);
+    case 15: return launch_split<2, 2, 4, 4, 2, 3, EPI, ODT>(p, grid_m, s);
+    case 16: return launch_split<2, 2, 2, 4, 3, 3, EPI, ODT>(p, grid_m, s);
     default: return launch_pipe<4, 4, 4, 1, 64, EPI, ODT>(p, grid_m, s);
   }
 }
