@@ -241,6 +241,31 @@ int moe_forward(const moe_config* cfg, int64_t T, const void* hidden, const void
 int moe_quantize_fp8_1x128(int64_t rows, int64_t cols, const void* in, int32_t in_dtype,
                            uint8_t* codes, float* scales, hipStream_t stream);
 
+/* Expert load of one routed batch (V3 lab page §4 balance check). */
+typedef struct moe_load_stats {
+  int32_t rows;   /* expert_offsets[E] - expert_offsets[0]                      */
+  int32_t min;    /* smallest per-expert count                                  */
+  int32_t max;    /* largest per-expert count                                   */
+  int32_t empty;  /* experts with no rows                                       */
+  float mean;     /* rows / E                                                   */
+  float cv;       /* std / mean, std with n - 1 (0 when E == 1 or rows == 0)    */
+} moe_load_stats;
+
+/*
+ * Auxiliary-loss-free balancing step and load statistics (DeepSeek V3/R1
+ * overview, xxqk.cn/news/389306, §2.2: the routing bias of an overloaded
+ * expert is lowered by a fixed step, that of an underloaded one raised; V3 lab
+ * page §4: per-expert counts, min, max and coefficient of variation).
+ *   expert_offsets [E+1] as produced by moe_permute (or moe_forward's opts)
+ *   bias   [E] fp32 e_score_correction_bias, updated in place, or NULL:
+ *          share = fp32(rows / E), b_e = fp32(b_e + gamma * sign(share - count_e))
+ *   gamma  step size, finite and >= 0
+ *   stats  one moe_load_stats in device memory, or NULL
+ * One kernel on `stream`; needs no workspace.  E <= 1024.
+ */
+int moe_load_balance(const moe_config* cfg, const int32_t* expert_offsets, float* bias, float gamma,
+                     moe_load_stats* stats, hipStream_t stream);
+
 /* Static text for a moe_status value. */
 const char* moe_strerror(int status);
 

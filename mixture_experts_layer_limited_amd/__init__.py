@@ -27,7 +27,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_CONFIG", -3: "MOE
           -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP"}
 
 EXPORTS = ("moe_workspace_size", "moe_validate_config", "moe_route", "moe_permute", "moe_grouped_swiglu",
-           "moe_combine", "moe_forward", "moe_quantize_fp8_1x128", "moe_strerror", "moe_version")
+           "moe_combine", "moe_forward", "moe_load_balance", "moe_quantize_fp8_1x128", "moe_strerror",
+           "moe_version")
 
 
 class MoeError(RuntimeError):
@@ -86,12 +87,13 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [cfgp, i64, vp, vp, vp, vp, vp, vp, vp]
         L.moe_forward.argtypes = [cfgp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                   ctypes.POINTER(ForwardOpts), vp, sz, vp]
+        L.moe_load_balance.argtypes = [cfgp, vp, vp, ctypes.c_float, vp, vp]
         L.moe_quantize_fp8_1x128.argtypes = [i64, i64, vp, i32, vp, vp, vp]
         L.moe_strerror.argtypes = [ctypes.c_int]
         L.moe_strerror.restype = ctypes.c_char_p
         L.moe_version.argtypes = []
         for name in ("moe_validate_config", "moe_route", "moe_permute", "moe_grouped_swiglu", "moe_combine",
-                     "moe_forward", "moe_quantize_fp8_1x128", "moe_version"):
+                     "moe_forward", "moe_load_balance", "moe_quantize_fp8_1x128", "moe_version"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -183,6 +185,29 @@ def forward(cfg, T, hidden, gate_w, bias, w13, w13_scales, w2, w2_scales, sh_w13
                              _ptr(w13_scales), _ptr(w2), _ptr(w2_scales), _ptr(sh_w13), _ptr(sh_w13_scales),
                              _ptr(sh_w2), _ptr(sh_w2_scales), _ptr(out), ctypes.byref(opts), wp, wb,
                              _stream(stream)), "moe_forward")
+
+
+class LoadStats(ctypes.Structure):
+    """moe_load_stats: expert load of one routed batch."""
+    _fields_ = [("rows", ctypes.c_int32), ("min", ctypes.c_int32), ("max", ctypes.c_int32),
+                ("empty", ctypes.c_int32), ("mean", ctypes.c_float), ("cv", ctypes.c_float)]
+
+
+LOAD_STATS_BYTES = ctypes.sizeof(LoadStats)
+
+
+def load_stats_from(buf: torch.Tensor) -> LoadStats:
+    """Decode the moe_load_stats a device byte buffer received."""
+    raw = bytes(buf.detach().cpu().numpy().tobytes()[:LOAD_STATS_BYTES])
+    return LoadStats.from_buffer_copy(raw)
+
+
+def load_balance(cfg: MoeConfig, expert_offsets: torch.Tensor, bias: Optional[torch.Tensor], gamma: float,
+                 stats: Optional[torch.Tensor], stream=None):
+    """moe_load_balance: bias [E] fp32 updated in place (or None); stats is a
+    device uint8 buffer of at least LOAD_STATS_BYTES (or None)."""
+    _check(lib().moe_load_balance(ctypes.byref(cfg), _ptr(expert_offsets), _ptr(bias), float(gamma), _ptr(stats),
+                                  _stream(stream)), "moe_load_balance")
 
 
 def quantize_fp8_1x128(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, stream=None):

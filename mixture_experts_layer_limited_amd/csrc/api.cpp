@@ -529,6 +529,16 @@ int moe_forward(const moe_config* c, int64_t T, const void* hidden, const void* 
   return MOE_OK;
 }
 
+int moe_load_balance(const moe_config* c, const int32_t* expert_offsets, float* bias, float gamma,
+                     moe_load_stats* stats, hipStream_t stream) {
+  MOE_TRY(check_cfg(c));
+  if (!expert_offsets) return MOE_ERR_INVALID_ARG;
+  if (!isfinite(gamma) || gamma < 0.0f) return MOE_ERR_INVALID_ARG;
+  if (!bias && !stats) return MOE_OK;
+  HIP_TRY(launch_load_balance(expert_offsets, c->n_experts, bias, gamma, stats, stream));
+  return MOE_OK;
+}
+
 int moe_quantize_fp8_1x128(int64_t rows, int64_t cols, const void* in, int32_t in_dtype, uint8_t* codes,
                            float* scales, hipStream_t stream) {
   if (rows < 0 || cols < 0 || (cols % 128)) return MOE_ERR_INVALID_ARG;

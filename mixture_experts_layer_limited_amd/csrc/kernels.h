@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "moe355.h"
+
 namespace moe {
 
 enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1, MOE_DT_FP8 = 2 };
@@ -88,6 +90,8 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 hipError_t launch_combine(int adt, int T, int H, int k, const void* expert_out, const float* acc,
                           const int32_t* inv, const float* topk_w, const void* shared_out, void* out,
                           hipStream_t s);
+hipError_t launch_load_balance(const int32_t* offsets, int E, float* bias, float gamma, ::moe_load_stats* stats,
+                               hipStream_t s);
 hipError_t launch_quantize(int in_dt, int64_t rows, int64_t cols, const void* in, uint8_t* codes,
                            float* scales, hipStream_t s);
 

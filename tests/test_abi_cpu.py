@@ -127,6 +127,11 @@ def test_entry_points_reject_before_launch():
     assert L.moe_forward(b(c), 16, p, p, null, p, null, p, null, p, null, p, null, p, b(opts), p, 1 << 40,
                          null) == -1      # bad epilogue
     assert L.moe_forward(b(c), 16, p, p, null, p, null, p, null, p, null, p, null, p, null, p, 8, null) == -4
+    assert L.moe_load_balance(b(c), null, p, ctypes.c_float(0.01), p, null) == -1      # no offsets
+    assert L.moe_load_balance(b(c), p, p, ctypes.c_float(-1.0), p, null) == -1        # negative step
+    assert L.moe_load_balance(b(c), p, p, ctypes.c_float(float("nan")), p, null) == -1
+    assert L.moe_load_balance(b(bad), p, p, ctypes.c_float(0.01), p, null) == -2
+    assert L.moe_load_balance(b(c), p, null, ctypes.c_float(0.01), null, null) == 0   # nothing to do
     assert L.moe_quantize_fp8_1x128(4, 100, p, 1, p, p, null) == -1
     assert L.moe_quantize_fp8_1x128(4, 128, p, 2, p, p, null) == -1
 

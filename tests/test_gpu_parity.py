@@ -361,3 +361,54 @@ def test_forward_full_size_sampled(name, samples):
     say(f"  max rel err {err:.3e} (tol {TOL[cfg.dtype]})")
     assert err <= TOL[cfg.dtype]
     assert bool(torch.isfinite(out.float()).all())
+
+
+# ----------------------------------------------------- load balance step ---
+
+def _ids_for(mode, T, E, k, rng):
+    if T == 0:
+        return np.zeros((0, k), dtype=np.int64)
+    if mode == "uniform":          # k distinct experts per token, uniformly
+        return np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)])
+    if mode == "skewed":           # Zipf-like preference, many empty experts
+        p = 1.0 / np.arange(1, E + 1) ** 1.1
+        p /= p.sum()
+        return np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)])
+    if mode == "one_expert":       # E = 1: cv is 0 by definition
+        return np.zeros((T, 1), dtype=np.int64)
+    raise ValueError(mode)
+
+
+@pytest.mark.parametrize("mode,T,E,k", [("uniform", 900, 256, 8), ("skewed", 128, 256, 8),
+                                        ("uniform", 77, 1024, 32), ("one_expert", 50, 1, 1),
+                                        ("uniform", 0, 64, 6)])
+def test_load_balance_matches_oracle(mode, T, E, k):
+    """Bias step bit-exact against the oracle's sign rule in fp32; load statistics
+    against the oracle's counts, min, max, empty (exact) and mean, cv (fp32)."""
+    say(f"load balance {mode} T={T} E={E} k={k}")
+    rng = np.random.default_rng(11)
+    ids = _ids_for(mode, T, E, k, rng).reshape(T, k)
+    off, _, _ = oracle.permute(ids, E)
+    cfgd = dict(hidden=128, inter=128, n_experts=E, top_k=k, dtype="bf16")
+    if E >= 8:
+        cfgd.update(n_group=8, topk_group=8)
+    c = moe.make_config(**cfgd)
+    bias0 = (rng.standard_normal(E) * 0.05).astype(np.float32)
+    gamma = np.float32(1e-3)
+    bias = torch.from_numpy(bias0).to(DEV)
+    stats = torch.zeros(moe.LOAD_STATS_BYTES, dtype=torch.uint8, device=DEV)
+    moe.load_balance(c, torch.from_numpy(off.astype(np.int32)).to(DEV), bias, float(gamma), stats)
+    torch.cuda.synchronize()
+    rows = int(off[-1])
+    share = np.float32(rows) / np.float32(E)
+    counts = np.diff(off)
+    want = oracle.bias_update(bias0.astype(np.float64), counts, np.full(E, share, np.float64),
+                              float(gamma)).astype(np.float32)
+    got = bias.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    st = moe.load_stats_from(stats)
+    ref = oracle.load_stats(ids, E)
+    say(f"  rows {st.rows} min {st.min} max {st.max} empty {st.empty} mean {st.mean:.3f} cv {st.cv:.4f}")
+    assert (st.rows, st.min, st.max, st.empty) == (rows, ref["min"], ref["max"], ref["empty"])
+    assert st.mean == pytest.approx(ref["mean"], rel=1e-7, abs=0)
+    assert st.cv == pytest.approx(ref["cv"], rel=1e-6, abs=1e-12)
