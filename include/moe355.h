@@ -148,6 +148,13 @@ int moe_validate_config(const moe_config* cfg);
  * Selection: c = fp32(s + b); for n_group > 1 a group scores
  * fp32(c_first + c_second) of its two largest c; the topk_group best groups
  * (ties to the lower group) are kept; the k best c in kept groups win.
+ * The router GEMM accumulates in fp32; given a workspace, for bf16 it may
+ * split H into slices whose partial logits (kept in ws) are added in slice
+ * order: the logits are deterministic for a given config and T, and those of
+ * moe_forward equal those of moe_route with a workspace.
+ *   ws         moe_workspace_size(cfg, T, MOE_OP_ROUTE) bytes; unused when
+ *              scores_in is given; optional when scores_out is given (NULL
+ *              keeps the router GEMM unsplit and writes the logits in place)
  */
 int moe_route(const moe_config* cfg, int64_t T, const void* hidden, const void* gate_w,
               const float* bias, const float* scores_in, float* scores_out,

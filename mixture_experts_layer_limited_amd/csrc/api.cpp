@@ -92,9 +92,29 @@ int max_mtiles(int64_t rows, int bm, int groups) {
 
 // ------------------------------------------------------------- workspace ---
 
+// K slices of the router GEMM: enough work-groups for the whole chip when T is
+// small (a divisor of H/64, at most 64).
+GemmShape router_shape(const moe_config* c, int64_t T) {
+  const int64_t eb = act_bytes(c);
+  return gemm_shape(2, act_dt(c), (int)T, T * c->hidden * eb, (int64_t)c->n_experts * c->hidden * eb);
+}
+
+int router_splits(const moe_config* c, int64_t T) {
+  const GemmShape sh = router_shape(c, T);
+  if (sh.kind < 10) return 1;  // only the pipelined kernel splits K
+  const int64_t tiles = ((T + sh.bm - 1) / sh.bm) * ((c->n_experts + sh.bn - 1) / sh.bn);
+  const int nk = c->hidden / 64;
+  int want = (int)((512 + tiles - 1) / tiles);
+  if (want > 64) want = 64;
+  int best = 1;
+  for (int d = 1; d <= nk && d <= want; ++d)
+    if (nk % d == 0) best = d;
+  return best;
+}
+
 struct RouteWs { float* logits; };
 void carve_route(Carver& cv, const moe_config* c, int64_t T, RouteWs& w) {
-  w.logits = cv.take<float>((size_t)T * c->n_experts);
+  w.logits = cv.take<float>((size_t)router_splits(c, T) * T * c->n_experts);
 }
 
 struct PermuteWs { int32_t* counts; };
@@ -170,6 +190,8 @@ struct ForwardWs {
 void carve_forward(Carver& cv, const moe_config* c, int64_t T, bool scatter, ForwardWs& w) {
   const int64_t rows = T * c->top_k;
   w.scores = cv.take<float>((size_t)T * c->n_experts);
+  if (router_splits(c, T) > 1) carve_route(cv, c, T, w.route);
+  else w.route.logits = nullptr;
   w.ids = cv.take<int32_t>((size_t)rows);
   w.topw = cv.take<float>((size_t)rows);
   w.offsets = cv.take<int32_t>((size_t)c->n_experts + 1);
@@ -209,21 +231,27 @@ int do_route(const moe_config* c, int64_t T, const void* hidden, const void* gat
     rp.scores_given = 1;
     rp.scores_out = nullptr;
   } else {
-    // Logits land where the scores go (in place per element), else in the workspace.
-    float* logits = scores_out ? scores_out : logits_ws;
+    // Logits land in the workspace (all K slices), or, unsplit, where the
+    // scores go (in place per element).
+    const int parts = logits_ws ? router_splits(c, T) : 1;
+    float* logits = (scores_out && parts == 1) ? scores_out : logits_ws;
     GemmParams g{};
     g.A = hidden; g.a_rows = nullptr;
     g.B = gate_w; g.b_gstride = 0;
     g.K = c->hidden; g.N = c->n_experts;
     g.C = logits;
     g.tiles = nullptr;
-    const GemmShape sh = gemm_shape(2, act_dt(c), (int)T, 0, 0);
+    g.ksplit = parts;
+    g.c_split_stride = T * c->n_experts;
+    const GemmShape sh = router_shape(c, T);
     g.M = (int)T;
     g.a_nrows = T;
     g.n_mtiles = (int)((T + sh.bm - 1) / sh.bm);
     g.ntn = (c->n_experts + sh.bn - 1) / sh.bn;
     HIP_TRY(launch_gemm(act_dt(c), EPI_STORE, MOE_DT_F32, g, sh, g.n_mtiles, s));
     rp.logits = logits;
+    rp.n_parts = parts;
+    rp.part_stride = T * c->n_experts;
     rp.scores_given = 0;
     rp.scores_out = scores_out;
   }
@@ -411,7 +439,9 @@ int moe_route(const moe_config* c, int64_t T, const void* hidden, const void* ga
   if (!scores_in && (!hidden || !gate_w)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   RouteWs w{};
-  if (!scores_in && !scores_out) {
+  // Without scores_out the logits need the workspace; with scores_out a
+  // workspace is optional and only enables the split-K router GEMM.
+  if (!scores_in && (!scores_out || ws)) {
     Carver probe(nullptr);
     carve_route(probe, c, T, w);
     MOE_TRY(check_ws(ws, ws_bytes, probe.used));
@@ -505,7 +535,7 @@ int moe_forward(const moe_config* c, int64_t T, const void* hidden, const void* 
   int32_t* inv = (opts && opts->inv_perm) ? opts->inv_perm : w.inv;
   const int64_t rows = T * c->top_k;
 
-  MOE_TRY(do_route(c, T, hidden, gate_w, bias, nullptr, scores, ids, topw, nullptr, stream));
+  MOE_TRY(do_route(c, T, hidden, gate_w, bias, nullptr, scores, ids, topw, w.route.logits, stream));
   HIP_TRY(launch_permute(ids, (int)rows, c->top_k, c->n_experts, w.perm.counts, offsets, src, inv, stream));
 
   // Shared expert first: its quantised activations (FP8) are reused by the routed experts.

@@ -300,7 +300,7 @@ static int tile_bn(int kind) { return kind >= 10 ? 256 : kTileBN[kind]; }
 // group's weights (the pipelined kernel addresses both with 31-bit offsets).
 GemmShape gemm_shape(int which, int dt, int rows_hint, int64_t a_bytes, int64_t b_bytes) {
   int kind;
-  if (which == 2) kind = 0;
+  if (which == 2) kind = dt == MOE_DT_BF16 ? 14 : 0;  // router: 64 x 256 tiles, split K
   else if (rows_hint <= 32) kind = dt == MOE_DT_BF16 ? 14 : 1;
   else if (rows_hint < 128) kind = dt == MOE_DT_BF16 ? 12 : 0;
   else kind = dt == MOE_DT_BF16 ? 15 : 0;

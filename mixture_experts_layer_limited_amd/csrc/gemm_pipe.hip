@@ -94,8 +94,11 @@ __global__ __launch_bounds__(256, OCC) void gemm_pipe_kernel(GemmParams p) {
   const int64_t krow = (int64_t)p.K * 2;  // bytes per A / B row
   const char* Bg = (const char*)p.B + (int64_t)grp * p.b_gstride * 2;
   const int b_nrows = (EPI == EPI_SWIGLU) ? 2 * p.N : p.N;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, p.a_nrows * krow);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bg, (int64_t)b_nrows * krow);
+  // split K: this group's slice starts kofs bytes into every row
+  const int nsplit = p.ksplit > 1 ? p.ksplit : 1;
+  const int64_t kofs = (int64_t)blockIdx.y * (krow / nsplit);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc((const char*)p.A + kofs, p.a_nrows * krow - kofs);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bg + kofs, (int64_t)b_nrows * krow - kofs);
 
   // Per-lane byte offsets of the rows this lane copies (fixed over K).
   // Lane l of a DMA instruction fills row (l / CPR), slot (l % CPR) of an RPI-row block.
@@ -123,7 +126,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_pipe_kernel(GemmParams p) {
     vob[i] = (uint32_t)((int64_t)wrow * krow + chunk * 16);
   }
 
-  const int nk = p.K * 2 / ROW;
+  const int nk = p.K * 2 / nsplit / ROW;
 
   // Issue the DMA of K step kt into ring slot kt % S; for kt >= nk the offset is
   // out of the buffers' range, so the hardware writes zeros without touching
@@ -234,10 +237,11 @@ __global__ __launch_bounds__(256, OCC) void gemm_pipe_kernel(GemmParams p) {
           if (col < p.N) atomicAdd((float*)p.C + (int64_t)tok * p.N + col, w * acc[i][j][e]);
         }
       } else {
+        typename Elem<ODT>::T* C = (typename Elem<ODT>::T*)p.C + (int64_t)blockIdx.y * p.c_split_stride;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int col = nt * BN + bblock(j) * 32 + lr;
-          if (col < p.N) Elem<ODT>::store((typename Elem<ODT>::T*)p.C, (int64_t)prow * p.N + col, acc[i][j][e]);
+          if (col < p.N) Elem<ODT>::store(C, (int64_t)prow * p.N + col, acc[i][j][e]);
         }
       }
     }
@@ -549,7 +553,8 @@ static hipError_t launch_pipe(const GemmParams& p, int grid_m, hipStream_t s) {
   }
   const int64_t grid = (int64_t)grid_m * p.ntn;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds_bytes, s, p);
+  const unsigned nsplit = p.ksplit > 1 ? (unsigned)p.ksplit : 1u;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid, nsplit), dim3(256), lds_bytes, s, p);
   return hipGetLastError();
 }
 

@@ -28,6 +28,10 @@ struct GemmParams {
   int M;                  // dense: rows
   int ntn;                // number of n-tiles
   int64_t a_nrows;        // rows of A (bounds of the activation buffer)
+  // Split K (pipelined single-ring kernel, store epilogue only): grid.y = ksplit
+  // slices of K / ksplit columns each; slice z writes C + z * c_split_stride.
+  int ksplit;             // 0 or 1: no split
+  int64_t c_split_stride; // elements between the slices' outputs
 };
 
 struct GemmShape {
@@ -70,7 +74,10 @@ GemmShape gemm_fp8_shape(int rows_hint, int64_t a_bytes, int64_t b_bytes);
 hipError_t launch_gemm_fp8(int epi, const GemmFp8Params& p, const GemmShape& g, int grid_m, hipStream_t s);
 
 struct RouteParams {
-  const float* logits;    // [T,E] router logits, or scores when scores_given
+  const float* logits;    // [T,E] router logits, or scores when scores_given;
+                          // n_parts > 1: partial logits of K slices, part_stride apart
+  int n_parts;
+  int64_t part_stride;
   int scores_given;
   const float* bias;      // [E] or NULL
   float* scores_out;      // [T,E] or NULL

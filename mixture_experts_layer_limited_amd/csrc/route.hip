@@ -33,6 +33,21 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(RouteParams p) 
     valid[i] = active && e < E;
     s[i] = valid[i] ? row[e] : 0.0f;
   }
+  // logits of a split-K router GEMM: partial sums of K slices, added in slice
+  // order (loads issued 8 slices at a time)
+  for (int q0 = 1; q0 < p.n_parts; q0 += 8) {
+    float part[8][V];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < V; ++i)
+        part[u][i] = (valid[i] && q0 + u < p.n_parts) ? row[(int64_t)(q0 + u) * p.part_stride + lane * V + i] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < V; ++i)
+        if (q0 + u < p.n_parts) s[i] += part[u][i];
+  }
 
   if (!p.scores_given) {
     if (p.scoring == 0) {  // softmax over all E experts

@@ -117,6 +117,18 @@ def test_route_from_hidden(name):
     differ = float((np.sort(own, 1) != np.sort(ids_ref, 1)).any(1).mean())
     say(f"  tokens whose fp64 routing picks another expert set: {differ:.4%}")
     assert differ < 0.01
+    # with a workspace the bf16 router GEMM splits H into slices (summed in order)
+    ws = moe.workspace(c, T, moe.MOE_OP_ROUTE)
+    scores2, ids2, w2 = f32((T, E)), i32((T, k)), f32((T, k))
+    moe.route(c, T, x, gw, bias, None, scores2, ids2, w2, ws)
+    torch.cuda.synchronize()
+    s2 = scores2.cpu().numpy()
+    err2 = np.abs(s2 - s_ref).max()
+    say(f"  split-K router: max |score - fp64 score| = {err2:.3g}")
+    assert err2 < 2e-5
+    ids2_ref, w2_ref = oracle_routing(cfg, s2, r["bias"])
+    assert np.array_equal(ids2.cpu().numpy(), ids2_ref)
+    np.testing.assert_allclose(w2.cpu().numpy(), w2_ref, rtol=2e-6, atol=1e-7)
 
 
 # ---------------------------------------------------------------- permute ---
@@ -300,7 +312,9 @@ def test_staged_calls_match_forward():
     c = binding_config(cfg)
     T, E, k, H, Is = cfg.tokens, cfg.n_experts, cfg.top_k, cfg.hidden, cfg.shared_inter
     scores, ids, w = f32((T, E)), i32((T, k)), f32((T, k))
-    moe.route(c, T, inp["x"], inp["gate_w"], inp["bias"], None, scores, ids, w)
+    # with a workspace, as moe_forward has one: the same split-K router GEMM
+    moe.route(c, T, inp["x"], inp["gate_w"], inp["bias"], None, scores, ids, w,
+              moe.workspace(c, T, moe.MOE_OP_ROUTE))
     off, src, inv = i32(E + 1), i32(T * k), i32(T * k)
     moe.permute(c, T, ids, off, src, inv, moe.workspace(c, T, moe.MOE_OP_PERMUTE))
     rows = torch.empty(T * k, H, dtype=torch.bfloat16, device=DEV)
