@@ -244,9 +244,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_kernel(GemmFp8Params p)
 // per row).  Weight-block scales are wave-uniform scalar loads, fetched one step
 // ahead.  Per step and 32x32 block: two 32x32x64 MFMAs into a zeroed partial,
 // then acc += partial * (sa[row] * sb).
-template <int TM, int TN, int SA, int SB, int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_fp8_split_kernel(GemmFp8Params p) {
-  constexpr int WM = 2, WN = 2, NW = 4;
+template <int WM, int WN, int TM, int TN, int SA, int SB, int EPI>
+__global__ __launch_bounds__(WM * WN * 64, 1) void gemm_fp8_split_kernel(GemmFp8Params p) {
+  constexpr int NW = WM * WN;
   constexpr int BM = WM * TM * 32;
   constexpr int BN = WN * TN * 32;
   constexpr int ROW = 128, CPR = 8, RPI = 8;
@@ -254,12 +254,12 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_split_kernel(GemmFp8Params p)
   constexpr int ASLOT = ADATA + NW * 256;     // + activation scales: 64 lanes x 4 B per wave
   constexpr int BSLOT = BN * ROW;
   constexpr int AI = BM / RPI / NW, BI = BN / RPI / NW;
-  constexpr int RW = BM / NW;                 // scale rows per wave (32 or 64)
+  constexpr int RW = BM / NW;                 // scale rows per wave (16, 32 or 64)
   constexpr int AL = AI + 1;                  // A instructions per wave per step (data + scales)
   constexpr int LI = AL + BI;
   constexpr int VMN = SB > SA ? BI + (SA - 2) * LI : (SA - 2) * LI;
   static_assert(AI * RPI * NW == BM && BI * RPI * NW == BN, "tile / wave mismatch");
-  static_assert(RW == 32 || RW == 64, "scale rows per wave");
+  static_assert(RW == 16 || RW == 32 || RW == 64, "scale rows per wave");
   static_assert(SA >= 2 && SB >= SA && VMN < 64, "ring depths");
   static_assert(EPI != EPI_SWIGLU || TN % 2 == 0, "SwiGLU pairs gate and up tiles");
 
@@ -386,7 +386,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_split_kernel(GemmFp8Params p)
   int tm_live = 0;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
-    if ((wm + 2 * i) * 32 < rows) tm_live = i + 1;
+    if ((wm + WM * i) * 32 < rows) tm_live = i + 1;
   tm_live = __builtin_amdgcn_readfirstlane(tm_live);
 
   const int lr = lane & 31, hi = lane >> 5;
@@ -414,7 +414,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_split_kernel(GemmFp8Params p)
       b[st_][j][1] = *(const u32x4*)(r_ + c1_);                                                     \
     }                                                                                               \
     _Pragma("unroll") for (int i = 0; i < NL; ++i) {                                                \
-      const char* r_ = sa_ + ((wm + 2 * i) * 32 + lr) * ROW;                                        \
+      const char* r_ = sa_ + ((wm + WM * i) * 32 + lr) * ROW;                                        \
       a[st_][i][0] = *(const u32x4*)(r_ + c0_);                                                     \
       a[st_][i][1] = *(const u32x4*)(r_ + c1_);                                                     \
     }                                                                                               \
@@ -442,7 +442,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_split_kernel(GemmFp8Params p)
     float sa[NL][16];                                                                                \
     _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                   \
       _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                                \
-        const int r_ = (wm + 2 * i) * 32 + 8 * q + 4 * hi;                                           \
+        const int r_ = (wm + WM * i) * 32 + 8 * q + 4 * hi;                                           \
         /* read as u32x4 like the fragments (no wait on the ring DMAs in flight) */                \
         const u32x4 u_ = *(const u32x4*)(sa_ + ADATA + ((r_ / RW) * 64 + r_ % RW) * 4);             \
         const float4 v_ = __builtin_bit_cast(float4, u_);                                            \
@@ -488,7 +488,7 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_split_kernel(GemmFp8Params p)
     if (i >= tm_live) continue;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int row = (wm + 2 * i) * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+      const int row = (wm + WM * i) * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
       if (row >= rows) continue;
       const int prow = r0 + row;
       if constexpr (EPI == EPI_SWIGLU) {
@@ -518,12 +518,12 @@ __global__ __launch_bounds__(256, 1) void gemm_fp8_split_kernel(GemmFp8Params p)
   }
 }
 
-template <int TM, int TN, int SA, int SB, int EPI>
+template <int WM, int WN, int TM, int TN, int SA, int SB, int EPI>
 static hipError_t launch8_split(const GemmFp8Params& p, int grid_m, hipStream_t s) {
-  constexpr int BM = 2 * TM * 32, BN = 2 * TN * 32;
-  constexpr int lds_bytes = SA * (BM * 128 + 1024) + SB * BN * 128;
+  constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
+  constexpr int lds_bytes = SA * (BM * 128 + WM * WN * 256) + SB * BN * 128;
   static_assert(lds_bytes <= 160 * 1024, "LDS");
-  auto kern = gemm_fp8_split_kernel<TM, TN, SA, SB, EPI>;
+  auto kern = gemm_fp8_split_kernel<WM, WN, TM, TN, SA, SB, EPI>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
@@ -532,7 +532,7 @@ static hipError_t launch8_split(const GemmFp8Params& p, int grid_m, hipStream_t 
   }
   const int64_t grid = (int64_t)grid_m * p.ntn;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds_bytes, s, p);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WM * WN * 64), lds_bytes, s, p);
   return hipGetLastError();
 }
 
@@ -541,7 +541,8 @@ static hipError_t launch8_split(const GemmFp8Params& p, int grid_m, hipStream_t 
 #endif
 
 // kind 0: register-staged 128 x 128 (any size); kind 1: pipelined 128 x 256
-// (A and B buffers addressed with 31-bit offsets)
+// (A and B buffers addressed with 31-bit offsets), 2 x 4 waves of 64 x 64: two
+// waves per SIMD, so one wave's scaled fold (VALU) overlaps the other's MFMAs
 GemmShape gemm_fp8_shape(int rows_hint, int64_t a_bytes, int64_t b_bytes) {
   GemmShape g;
   (void)rows_hint;
@@ -573,9 +574,9 @@ static hipError_t launch8(const GemmFp8Params& p, int grid_m, hipStream_t s) {
 hipError_t launch_gemm_fp8(int epi, const GemmFp8Params& p, const GemmShape& g, int grid_m, hipStream_t s) {
   if (g.kind == 1) {
     switch (epi) {
-      case EPI_SWIGLU: return launch8_split<2, 4, 3, 3, EPI_SWIGLU>(p, grid_m, s);
-      case EPI_SCATTER: return launch8_split<2, 4, 3, 3, EPI_SCATTER>(p, grid_m, s);
-      case EPI_STORE: return launch8_split<2, 4, 3, 3, EPI_STORE>(p, grid_m, s);
+      case EPI_SWIGLU: return launch8_split<2, 4, 2, 2, 3, 3, EPI_SWIGLU>(p, grid_m, s);
+      case EPI_SCATTER: return launch8_split<2, 4, 2, 2, 3, 3, EPI_SCATTER>(p, grid_m, s);
+      case EPI_STORE: return launch8_split<2, 4, 2, 2, 3, 3, EPI_STORE>(p, grid_m, s);
       default: return hipErrorInvalidValue;
     }
   }
