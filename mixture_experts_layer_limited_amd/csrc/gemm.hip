@@ -276,24 +276,28 @@ static hipError_t launch_cfg(const GemmParams& p, int grid_m, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Tile shapes (kind: WMxWN waves, each TMxTN tiles of 32x32 -> BM x BN):
-//   0: 2x2 waves, 2x2 tiles -> 128 x 128      1: 1x4 waves, 1x2 tiles ->  32 x 256
-//   2: 2x2 waves, 4x4 tiles -> 256 x 256      3: 2x2 waves, 4x2 tiles -> 256 x 128
-//   4: 2x2 waves, 2x4 tiles -> 128 x 256      5: 1x4 waves, 2x2 tiles ->  64 x 256
+// Tile shapes by kind.  Register-staged kernel (fp32, and bf16 buffers past 2 GiB):
+//   0: 2x2 waves of 2x2 32x32 blocks -> 128 x 128;  1: 1x4 waves of 1x2 -> 32 x 256.
+// Pipelined bf16 kernels (gemm_pipe.hip): 12: 128 x 256 single ring; 14: 64 x 256
+// single ring (decode-sized groups and the split-K router); 15: 256 x 256 split
+// rings (prefill-sized groups).  MOE_TILE_GEMM1 / MOE_TILE_GEMM2 force a kind for
+// the gate/up or down GEMM at build time (tuning).
 #ifndef MOE_TILE_GEMM1
 #define MOE_TILE_GEMM1 -1
 #endif
 #ifndef MOE_TILE_GEMM2
 #define MOE_TILE_GEMM2 -1
 #endif
-static const int kTileBM[6] = {128, 32, 256, 256, 128, 64};
-static const int kTileBN[6] = {128, 256, 256, 128, 256, 256};
-// pipelined kernels (bf16 only): 10, 11, 15: 256 x 256; 12, 13, 16: 128 x 256; 14: 64 x 256
 static int tile_bm(int kind) {
-  if (kind < 10) return kTileBM[kind];
-  return (kind <= 11 || kind == 15) ? 256 : (kind <= 13 || kind == 16) ? 128 : 64;
+  switch (kind) {
+    case 1: return 32;
+    case 12: return 128;
+    case 14: return 64;
+    case 15: return 256;
+    default: return 128;
+  }
 }
-static int tile_bn(int kind) { return kind >= 10 ? 256 : kTileBN[kind]; }
+static int tile_bn(int kind) { return kind == 0 ? 128 : 256; }
 
 // which: 0 = gate/up GEMM, 1 = down GEMM, 2 = router GEMM.  rows_hint = mean
 // rows per group; a_bytes / b_bytes = sizes of the activation buffer and of one
@@ -307,6 +311,7 @@ GemmShape gemm_shape(int which, int dt, int rows_hint, int64_t a_bytes, int64_t 
   const bool pipe_ok = dt == MOE_DT_BF16 && a_bytes < (1LL << 31) && b_bytes < (1LL << 31);
   if (which == 0 && MOE_TILE_GEMM1 >= 0) kind = MOE_TILE_GEMM1;
   if (which == 1 && MOE_TILE_GEMM2 >= 0) kind = MOE_TILE_GEMM2;
+  if (kind != 0 && kind != 1 && kind != 12 && kind != 14 && kind != 15) kind = 0;
   if (kind >= 10 && !pipe_ok) kind = 0;
   GemmShape g;
   g.kind = kind;
@@ -317,14 +322,8 @@ GemmShape gemm_shape(int which, int dt, int rows_hint, int64_t a_bytes, int64_t 
 
 template <int DT, int EPI, int ODT>
 static hipError_t dispatch_shape(const GemmParams& p, const GemmShape& g, int grid_m, hipStream_t s) {
-  switch (g.kind) {
-    case 1: return launch_cfg<DT, 1, 4, 1, 2, EPI, ODT>(p, grid_m, s);
-    case 2: return launch_cfg<DT, 2, 2, 4, 4, EPI, ODT>(p, grid_m, s);
-    case 3: return launch_cfg<DT, 2, 2, 4, 2, EPI, ODT>(p, grid_m, s);
-    case 4: return launch_cfg<DT, 2, 2, 2, 4, EPI, ODT>(p, grid_m, s);
-    case 5: return launch_cfg<DT, 1, 4, 2, 2, EPI, ODT>(p, grid_m, s);
-    default: return launch_cfg<DT, 2, 2, 2, 2, EPI, ODT>(p, grid_m, s);
-  }
+  if (g.kind == 1) return launch_cfg<DT, 1, 4, 1, 2, EPI, ODT>(p, grid_m, s);
+  return launch_cfg<DT, 2, 2, 2, 2, EPI, ODT>(p, grid_m, s);
 }
 
 template <int DT, int EPI>

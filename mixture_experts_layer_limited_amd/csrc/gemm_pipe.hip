@@ -558,23 +558,16 @@ static hipError_t launch_pipe(const GemmParams& p, int grid_m, hipStream_t s) {
   return hipGetLastError();
 }
 
-// kind 10: 256 x 256, 64-byte rows, 4-slot ring
-// kind 11: 256 x 256, 128-byte rows, 2-slot ring
-// kind 12: 128 x 256, 128-byte rows, 3-slot ring
-// kind 13: 128 x 256, 64-byte rows, 6-slot ring
-// kind 14:  64 x 256, 128-byte rows, 4-slot ring
-// kind 15: 256 x 256 split rings, A 2 slots + B 3 slots (160 KB)
-// kind 16: 128 x 256 split rings, A 3 slots + B 3 slots
+// kind 12: 128 x 256, single ring of 3 slots of 128-byte K rows
+// kind 14:  64 x 256, single ring of 4 slots of 128-byte K rows (split K allowed)
+// kind 15: 256 x 256, split rings (A 2 slots + B 3 slots, 160 KB)
 template <int EPI, int ODT>
 static hipError_t pipe_kind(const GemmParams& p, const GemmShape& g, int grid_m, hipStream_t s) {
   switch (g.kind) {
-    case 11: return launch_pipe<4, 4, 2, 1, 128, EPI, ODT>(p, grid_m, s);
     case 12: return launch_pipe<2, 4, 3, 1, 128, EPI, ODT>(p, grid_m, s);
-    case 13: return launch_pipe<2, 4, 6, 1, 64, EPI, ODT>(p, grid_m, s);
     case 14: return launch_pipe<1, 4, 4, 1, 128, EPI, ODT>(p, grid_m, s);
     case 15: return launch_split<2, 2, 4, 4, 2, 3, EPI, ODT>(p, grid_m, s);
-    case 16: return launch_split<2, 2, 2, 4, 3, 3, EPI, ODT>(p, grid_m, s);
-    default: return launch_pipe<4, 4, 4, 1, 64, EPI, ODT>(p, grid_m, s);
+    default: return hipErrorInvalidValue;
   }
 }
 
