@@ -202,15 +202,19 @@ def main():
 
     eb = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.dtype]
     ab = 4 if cfg.dtype == "f32" else 2
-    rows = T * k
+    # With the routed experts' width, stored rows and T <= 1024, the shared expert runs
+    # as one more group of the routed GEMM launches, so the timed grouped GEMMs include it.
+    merged = Is == I and Is > 0 and a.epilogue == "store" and E < 1024 and T <= 1024
+    groups = non_empty + (1 if merged else 0)
+    rows = T * k + (T if merged else 0)
     flops1 = 2.0 * rows * (2 * I) * H
     flops2 = 2.0 * rows * H * I
-    # algorithmic bytes: weights of the experts that received rows, activations in, results out
-    bytes1 = non_empty * 2 * I * H * eb + T * H * ab + rows * I * ab
-    bytes2 = non_empty * H * I * eb + rows * I * ab + rows * H * ab
+    # algorithmic bytes: weights of the groups that received rows, activations in, results out
+    bytes1 = groups * 2 * I * H * eb + T * H * ab + rows * I * ab
+    bytes2 = groups * H * I * eb + rows * I * ab + rows * H * ab
     if cfg.dtype == "fp8":
-        bytes1 += non_empty * (2 * I // 128) * (H // 128) * 4 + T * (H // 128) * 4
-        bytes2 += non_empty * (H // 128) * (I // 128) * 4
+        bytes1 += groups * (2 * I // 128) * (H // 128) * 4 + T * (H // 128) * 4
+        bytes2 += groups * (H // 128) * (I // 128) * 4
     peak = PEAK_TFLOPS[cfg.dtype]
     ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
     intensity = flops1 / bytes1
@@ -222,7 +226,8 @@ def main():
         achieved = flops1 / (g1 * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak}
     roof.update({"traffic": measured_traffic(cfg.name),
-                 "kernel": "routed gate/up grouped GEMM with the SiLU*up epilogue",
+                 "kernel": "gate/up grouped GEMM with the SiLU*up epilogue (routed experts"
+                           + (" + the shared expert as one more group)" if merged else ")"),
                  "ms": g1, "algorithmic_bytes": bytes1, "algorithmic_flops": flops1})
     gg_tflops = (flops1 + flops2) / ((g1 + g2) * 1e-3) / 1e12
     result = {
@@ -242,7 +247,8 @@ def main():
                                f"{cfg.scoring} shared Is={Is}", "tokens": T, "hidden": H, "experts": E,
                    "inter": I, "top_k": k, "shared_inter": Is, "epilogue": a.epilogue,
                    "non_empty_experts": non_empty},
-        "grouped_gemm": {"ms_gate_up": g1, "ms_down": g2, "tflops": gg_tflops, "peak_tflops": peak,
+        "grouped_gemm": {"ms_gate_up": g1, "ms_down": g2, "shared_expert_included": merged,
+                         "tflops": gg_tflops, "peak_tflops": peak,
                          "frac_mfma_peak": gg_tflops / peak,
                          "gb_s": (bytes1 + bytes2) / ((g1 + g2) * 1e-3) / 1e9},
         "roofline": roof,

@@ -121,7 +121,9 @@ typedef struct moe_forward_opts {
   /* Timing hooks: events the caller created with hipEventCreate; any may be
    * NULL.  events[0]/[1] are recorded on `stream` right before/after the
    * routed experts' gate/up GEMM (with its SiLU*up epilogue), events[2]/[3]
-   * right before/after their down GEMM. */
+   * right before/after their down GEMM.  When shared_inter == inter, E < 1024,
+   * T <= 1024 and the rows are stored, the shared expert runs as one more group
+   * of these two launches, so the events bracket it too. */
   hipEvent_t events[4];
 } moe_forward_opts;
 

@@ -178,6 +178,19 @@ void carve_swiglu(Carver& cv, const moe_config* c, int64_t T, int64_t rows, int 
   w.row_w = scatter ? cv.take<float>((size_t)rows) : nullptr;
 }
 
+// The shared expert runs as group E of the routed launch (no launches of its
+// own, no separate output) when it has the routed experts' width, the routed
+// rows are stored rather than scatter-added, and T is small: a dense launch of
+// at most 4 x I/128 tiles of 256 rows cannot fill the chip, while for large T
+// the separate dense launch keeps its activation rows in L2 better than the
+// expert-ordered grouped launch does.
+constexpr int64_t kMergeSharedMaxT = 1024;
+bool merge_shared(const moe_config* c, int64_t T, bool scatter) {
+  // E + 1 groups must fit the tile builder's one-thread-per-group scan (1024)
+  return !scatter && c->shared_inter > 0 && c->shared_inter == c->inter && c->n_experts < 1024 &&
+         T <= kMergeSharedMaxT;
+}
+
 struct ForwardWs {
   RouteWs route;
   PermuteWs perm;
@@ -194,19 +207,21 @@ void carve_forward(Carver& cv, const moe_config* c, int64_t T, bool scatter, For
   else w.route.logits = nullptr;
   w.ids = cv.take<int32_t>((size_t)rows);
   w.topw = cv.take<float>((size_t)rows);
-  w.offsets = cv.take<int32_t>((size_t)c->n_experts + 1);
-  w.src = cv.take<int32_t>((size_t)rows);
+  const bool merged = merge_shared(c, T, scatter);
+  const int64_t rows_all = rows + (merged ? T : 0);
+  w.offsets = cv.take<int32_t>((size_t)c->n_experts + 2);
+  w.src = cv.take<int32_t>((size_t)rows_all);
   w.inv = cv.take<int32_t>((size_t)rows);
   carve_permute(cv, c, T, w.perm);
-  carve_swiglu(cv, c, T, rows, c->n_experts, c->inter, true, scatter, w.routed);
+  carve_swiglu(cv, c, T, rows_all, c->n_experts + (merged ? 1 : 0), c->inter, true, scatter, w.routed);
   if (scatter) {
     w.y = nullptr;
     w.acc = cv.take<float>((size_t)T * c->hidden);
   } else {
-    w.y = cv.take<char>((size_t)rows * c->hidden * act_bytes(c));
+    w.y = cv.take<char>((size_t)rows_all * c->hidden * act_bytes(c));
     w.acc = nullptr;
   }
-  if (c->shared_inter > 0) {
+  if (c->shared_inter > 0 && !merged) {
     carve_swiglu(cv, c, T, T, 1, c->shared_inter, false, false, w.shared);
     w.sh_out = cv.take<char>((size_t)T * c->hidden * act_bytes(c));
   } else {
@@ -270,13 +285,20 @@ void set_tiles(P& p, bool dense, int64_t rows, int bm, const int4* tiles, const 
   }
 }
 
+// Weights of the shared expert when it runs as one more group of the routed launch.
+struct SharedGroup {
+  const void* w13; const float* w13_s;
+  const void* w2; const float* w2_s;
+  int group;
+};
+
 // One grouped SwiGLU: routed experts (offsets given) or a dense FFN over all
 // rows (offsets == nullptr, the shared expert).
 int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, const void* hidden,
               const float* hidden_scales, const int32_t* src, const int32_t* offsets, const void* w13,
               const float* w13_s, const void* w2, const float* w2_s, int epi, const float* topk_w,
               const int32_t* inv, void* out, float* acc, const SwigluWs& w, hipStream_t s,
-              hipEvent_t const* ev = nullptr) {
+              hipEvent_t const* ev = nullptr, const SharedGroup* sg = nullptr) {
   auto mark = [&](int i) -> int {
     if (ev && ev[i]) return hip_status(hipEventRecord(ev[i], s));
     return MOE_OK;
@@ -302,6 +324,7 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
     p.A = xq; p.a_scales = xs; p.a_rows = src;
     p.B = (const uint8_t*)w13; p.b_scales = w13_s;
     p.b_gstride = (int64_t)2 * I * H; p.bs_gstride = (int64_t)(2 * I / 128) * (H / 128);
+    if (sg) { p.B2 = (const uint8_t*)sg->w13; p.b2_scales = sg->w13_s; p.b2_group = sg->group; }
     p.K = H; p.N = I;
     p.C = w.h;
     p.a_nrows = T;
@@ -316,6 +339,7 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
     q.A = w.hq; q.a_scales = w.h_scales; q.a_rows = nullptr;
     q.B = (const uint8_t*)w2; q.b_scales = w2_s;
     q.b_gstride = (int64_t)H * I; q.bs_gstride = (int64_t)(H / 128) * (I / 128);
+    if (sg) { q.B2 = (const uint8_t*)sg->w2; q.b2_scales = sg->w2_s; q.b2_group = sg->group; }
     q.K = I; q.N = H;
     q.a_nrows = rows;
     set_tiles(q, dense, rows, g2.bm, w.tiles2, w.ntiles2);
@@ -345,6 +369,7 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
   GemmParams p{};
   p.A = hidden; p.a_rows = src;
   p.B = w13; p.b_gstride = (int64_t)2 * I * H;
+  if (sg) { p.B2 = sg->w13; p.b2_group = sg->group; }
   p.K = H; p.N = I; p.C = w.h;
   p.a_nrows = T;
   set_tiles(p, dense, rows, g1.bm, w.tiles1, w.ntiles1);
@@ -356,6 +381,7 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
   GemmParams q{};
   q.A = w.h; q.a_rows = nullptr;
   q.B = w2; q.b_gstride = (int64_t)H * I;
+  if (sg) { q.B2 = sg->w2; q.b2_group = sg->group; }
   q.K = I; q.N = H;
   q.a_nrows = rows;
   set_tiles(q, dense, rows, g2.bm, w.tiles2, w.ntiles2);
@@ -527,16 +553,30 @@ int moe_forward(const moe_config* c, int64_t T, const void* hidden, const void* 
   Carver cv(ws);
   carve_forward(cv, c, T, scatter, w);
 
+  const bool merged = merge_shared(c, T, scatter);
+  const int E = c->n_experts;
   float* scores = (opts && opts->scores) ? opts->scores : w.scores;
   int32_t* ids = (opts && opts->topk_ids) ? opts->topk_ids : w.ids;
   float* topw = (opts && opts->topk_w) ? opts->topk_w : w.topw;
-  int32_t* offsets = (opts && opts->expert_offsets) ? opts->expert_offsets : w.offsets;
-  int32_t* src = (opts && opts->permuted_src) ? opts->permuted_src : w.src;
+  // merged: the permutation is extended by the shared group, so it lives in the
+  // workspace and is copied out when asked for
+  int32_t* offsets = (!merged && opts && opts->expert_offsets) ? opts->expert_offsets : w.offsets;
+  int32_t* src = (!merged && opts && opts->permuted_src) ? opts->permuted_src : w.src;
   int32_t* inv = (opts && opts->inv_perm) ? opts->inv_perm : w.inv;
   const int64_t rows = T * c->top_k;
+  const int64_t rows_all = rows + (merged ? T : 0);
 
   MOE_TRY(do_route(c, T, hidden, gate_w, bias, nullptr, scores, ids, topw, w.route.logits, stream));
-  HIP_TRY(launch_permute(ids, (int)rows, c->top_k, c->n_experts, w.perm.counts, offsets, src, inv, stream));
+  HIP_TRY(launch_permute(ids, (int)rows, c->top_k, E, w.perm.counts, offsets, src, inv, stream));
+  if (merged) {
+    HIP_TRY(launch_extend_shared(offsets, E, (int)rows, (int)T, src, stream));
+    if (opts && opts->expert_offsets)
+      HIP_TRY(hipMemcpyAsync(opts->expert_offsets, offsets, (size_t)(E + 1) * sizeof(int32_t),
+                             hipMemcpyDeviceToDevice, stream));
+    if (opts && opts->permuted_src)
+      HIP_TRY(hipMemcpyAsync(opts->permuted_src, src, (size_t)rows * sizeof(int32_t), hipMemcpyDeviceToDevice,
+                             stream));
+  }
 
   // Shared expert first: its quantised activations (FP8) are reused by the routed experts.
   const float* xs = nullptr;
@@ -546,16 +586,19 @@ int moe_forward(const moe_config* c, int64_t T, const void* hidden, const void* 
     xin = w.routed.xq;
     xs = w.routed.xs;
   }
-  if (c->shared_inter > 0) {
+  if (c->shared_inter > 0 && !merged) {
     moe_config sc = *c;
     sc.n_experts = 1; sc.top_k = 1; sc.inter = c->shared_inter; sc.n_group = 1; sc.topk_group = 1;
     MOE_TRY(do_swiglu(&sc, T, T, 1, c->shared_inter, xin, xs, nullptr, nullptr, sh_w13, sh_w13_scales, sh_w2,
                       sh_w2_scales, MOE_EPI_STORE_ROWS, nullptr, nullptr, w.sh_out, nullptr, w.shared, stream));
   }
   if (scatter) HIP_TRY(launch_fill_zero(w.acc, T * c->hidden, stream));
-  MOE_TRY(do_swiglu(c, T, rows, c->n_experts, c->inter, xin, xs, src, offsets, w13, w13_scales, w2, w2_scales, epi,
-                    topw, inv, w.y, w.acc, w.routed, stream, opts ? opts->events : nullptr));
-  HIP_TRY(launch_combine(act_dt(c), (int)T, c->hidden, c->top_k, w.y, w.acc, inv, topw, w.sh_out, out, stream));
+  const SharedGroup sg{sh_w13, sh_w13_scales, sh_w2, sh_w2_scales, E};
+  MOE_TRY(do_swiglu(c, T, rows_all, E + (merged ? 1 : 0), c->inter, xin, xs, src, offsets, w13, w13_scales, w2,
+                    w2_scales, epi, topw, inv, w.y, w.acc, w.routed, stream, opts ? opts->events : nullptr,
+                    merged ? &sg : nullptr));
+  const void* shared_rows = merged ? (const void*)((const char*)w.y + rows * c->hidden * act_bytes(c)) : w.sh_out;
+  HIP_TRY(launch_combine(act_dt(c), (int)T, c->hidden, c->top_k, w.y, w.acc, inv, topw, shared_rows, out, stream));
   return MOE_OK;
 }
 

@@ -119,13 +119,26 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
 // ----------------------------------------------------- workgroup mapping ---
 
 // Work-groups are handed to the 8 XCDs round-robin by id.  Remap a physical id
-// P in [0, n) to a logical id so that consecutive logical ids land on the same
-// XCD (and share its L2).
+// P in [0, n) to a logical id so that runs of MOE_XCD_CHUNK consecutive logical
+// ids land on one XCD (and share its L2), the runs going to the XCDs in turn;
+// the last partial round keeps the hardware order.  MOE_XCD_CHUNK 0: one
+// contiguous range per XCD.
+#ifndef MOE_XCD_CHUNK
+#define MOE_XCD_CHUNK 0
+#endif
 __device__ __forceinline__ int xcd_remap(int P, int n) {
   constexpr int kXcd = 8;
-  int q = n / kXcd, r = n % kXcd;
-  int x = P % kXcd, local = P / kXcd;
-  return x * q + (x < r ? x : r) + local;
+  if constexpr (MOE_XCD_CHUNK > 0) {
+    constexpr int C = MOE_XCD_CHUNK;
+    const int full = n / (kXcd * C) * (kXcd * C);
+    if (P >= full) return P;
+    const int x = P % kXcd, local = P / kXcd;
+    return ((local / C) * kXcd + x) * C + local % C;
+  } else {
+    int q = n / kXcd, r = n % kXcd;
+    int x = P % kXcd, local = P / kXcd;
+    return x * q + (x < r ? x : r) + local;
+  }
 }
 
 }  // namespace moe

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
   }
   const int rows = r1 - r0;
   const int64_t kbytes = (int64_t)p.K * EB;
-  const char* Bg = (const char*)p.B + (int64_t)grp * p.b_gstride * EB;
+  const char* Bg = (p.B2 && grp == p.b2_group) ? (const char*)p.B2 : (const char*)p.B + (int64_t)grp * p.b_gstride * EB;
 
   // Global source of every chunk this thread copies (fixed over the K loop).
   const char* aptr[CA];

@@ -63,8 +63,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_kernel(GemmFp8Params p)
   const int rows = r1 - r0;
   const int64_t K = p.K;
   const int nkb = p.K / 128;
-  const uint8_t* Bg = p.B + (int64_t)grp * p.b_gstride;
-  const float* SBg = p.b_scales + (int64_t)grp * p.bs_gstride;
+  const bool g2_ = p.B2 && grp == p.b2_group;
+  const uint8_t* Bg = g2_ ? p.B2 : p.B + (int64_t)grp * p.b_gstride;
+  const float* SBg = g2_ ? p.b2_scales : p.b_scales + (int64_t)grp * p.bs_gstride;
 
   const uint8_t* aptr[CA];
   bool aok[CA];
@@ -286,10 +287,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_fp8_split_kernel(GemmFp8
   const int rows = r1 - r0;
   const int64_t krow = p.K;  // bytes per A / B row
   const int nkb = p.K / 128;
-  const uint8_t* Bg = p.B + (int64_t)grp * p.b_gstride;
+  const bool g2_ = p.B2 && grp == p.b2_group;
+  const uint8_t* Bg = g2_ ? p.B2 : p.B + (int64_t)grp * p.b_gstride;
   // weight scales are read-only for the kernel's lifetime: constant address
   // space, so the wave-uniform loads below become scalar loads
-  const cfloat* SBg = (const cfloat*)(p.b_scales + (int64_t)grp * p.bs_gstride);
+  const cfloat* SBg = (const cfloat*)(g2_ ? p.b2_scales : p.b_scales + (int64_t)grp * p.bs_gstride);
   const int b_nrows = (EPI == EPI_SWIGLU) ? 2 * p.N : p.N;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, p.a_nrows * krow);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.a_scales, p.a_nrows * nkb * 4);

@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_pipe_kernel(GemmParams p) {
   }
   const int rows = r1 - r0;
   const int64_t krow = (int64_t)p.K * 2;  // bytes per A / B row
-  const char* Bg = (const char*)p.B + (int64_t)grp * p.b_gstride * 2;
+  const char* Bg = (p.B2 && grp == p.b2_group) ? (const char*)p.B2 : (const char*)p.B + (int64_t)grp * p.b_gstride * 2;
   const int b_nrows = (EPI == EPI_SWIGLU) ? 2 * p.N : p.N;
   // split K: this group's slice starts kofs bytes into every row
   const int nsplit = p.ksplit > 1 ? p.ksplit : 1;
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_split_kernel(GemmParams 
   }
   const int rows = r1 - r0;
   const int64_t krow = (int64_t)p.K * 2;
-  const char* Bg = (const char*)p.B + (int64_t)grp * p.b_gstride * 2;
+  const char* Bg = (p.B2 && grp == p.b2_group) ? (const char*)p.B2 : (const char*)p.B + (int64_t)grp * p.b_gstride * 2;
   const int b_nrows = (EPI == EPI_SWIGLU) ? 2 * p.N : p.N;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, p.a_nrows * krow);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bg, (int64_t)b_nrows * krow);

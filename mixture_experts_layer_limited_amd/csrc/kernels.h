@@ -17,6 +17,8 @@ struct GemmParams {
   const int32_t* a_rows;  // src(p) = a_rows[p]; NULL: src(p) = p
   const void* B;          // weights of group g at B + g * b_gstride elements, (out, in)
   int64_t b_gstride;
+  const void* B2;         // if not NULL: the weights of group b2_group (the shared expert
+  int b2_group;           // run as one more group of the routed launch)
   int K;                  // reduction length (elements)
   int N;                  // output columns; SwiGLU: h columns (B holds 2N rows)
   void* C;                // output: rows p (store, SwiGLU) or rows c_rows[p] (scatter)
@@ -58,6 +60,9 @@ struct GemmFp8Params {
   const float* b_scales;  // group g: b_scales + g * bs_gstride, [Nrows/128, K/128]
   int64_t b_gstride;      // bytes between groups
   int64_t bs_gstride;     // floats between groups
+  const uint8_t* B2;      // if not NULL: codes and scales of group b2_group
+  const float* b2_scales;
+  int b2_group;
   int K;
   int N;
   void* C;                // SwiGLU: bf16 h [rows, N]; store: bf16 [rows, N]; scatter: fp32 [T, N]
@@ -91,6 +96,8 @@ hipError_t launch_route(const RouteParams& p, hipStream_t s);
 hipError_t launch_permute(const int32_t* ids, int n, int k, int E, int32_t* counts, int32_t* offsets,
                           int32_t* src, int32_t* inv, hipStream_t s);
 int permute_blocks(int n);
+// offsets[E+1] = rows + T and src[rows + t] = t: the shared expert as group E.
+hipError_t launch_extend_shared(int32_t* offsets, int E, int rows, int T, int32_t* src, hipStream_t s);
 
 hipError_t launch_row_weights(const float* topk_w, const int32_t* inv, int n, float* row_w, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);

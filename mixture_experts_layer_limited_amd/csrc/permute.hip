@@ -112,3 +112,22 @@ hipError_t launch_permute(const int32_t* ids, int n, int k, int E, int32_t* coun
 }
 
 }  // namespace moe
+
+namespace moe {
+
+// The shared expert as group E of the routed launch: rows [rows, rows + T) of the
+// permuted order are the tokens themselves, and the group ends at rows + T.
+__global__ __launch_bounds__(256) void extend_shared_kernel(int32_t* __restrict__ offsets, int E, int rows, int T,
+                                                           int32_t* __restrict__ src) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t < T) src[rows + t] = t;
+  if (t == 0) offsets[E + 1] = rows + T;
+}
+
+hipError_t launch_extend_shared(int32_t* offsets, int E, int rows, int T, int32_t* src, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(extend_shared_kernel, dim3((T + 255) / 256), dim3(256), 0, s, offsets, E, rows, T, src);
+  return hipGetLastError();
+}
+
+}  // namespace moe
