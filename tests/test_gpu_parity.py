@@ -210,6 +210,12 @@ SMALL = {
     "v3_small_t1": _reduced("v3_prefill_bf16", tokens=1, hidden=1024, inter=256, n_experts=64, shared_inter=256),
     # about 300 rows per expert: the 256-row tiles, two ragged m-tiles per expert
     "v3_mid": _reduced("v3_prefill_bf16", tokens=1203, hidden=512, inter=384, n_experts=32, shared_inter=128),
+    # H and I not multiples of the 256-wide n-tiles; shared expert as one more group
+    "odd_dims": _reduced("v3_prefill_bf16", tokens=333, hidden=576, inter=192, n_experts=16, n_group=4,
+                         topk_group=2, top_k=4, shared_inter=192),
+    # shared expert of the routed width at T > 1024: its own dense launches
+    "wide_shared_large_t": _reduced("v3_prefill_bf16", tokens=1100, hidden=512, inter=256, n_experts=32,
+                                    shared_inter=256),
     "fp8_small": _reduced("v3_fp8", tokens=300, hidden=1024, inter=256, n_experts=64, shared_inter=256),
     "fp8_small_ragged": _reduced("v3_fp8", tokens=45, hidden=512, inter=384, n_experts=64, shared_inter=128),
 }
