@@ -24,6 +24,10 @@
  *     [I,2I); w2 (E,H,I); shared gate_up (2Is,H) split the same way; shared
  *     down (H,Is) (walkthrough §2.2-§2.3 stacked storage, §3.3 x @ w.T);
  *   - index tensors are int32; T*k < 2^31;
+ *   - activation, weight and output tensors (hidden, gate_w, w13, w2, sh_w13,
+ *     sh_w2, expert_out, acc, shared_out, out, quantiser input) start on a
+ *     16-byte boundary, E4M3 code outputs on an 8-byte boundary, every other
+ *     array on a 4-byte boundary (MOE_ERR_INVALID_ARG otherwise);
  *   - arguments are validated before anything is launched; a failed check
  *     returns a negative moe_status and launches nothing; T == 0 returns MOE_OK
  *     and launches nothing; a failed launch returns MOE_ERR_HIP (the HIP error

@@ -69,6 +69,13 @@ int check_T(const moe_config* c, int64_t T) {
   return MOE_OK;
 }
 
+// Activation, weight and output tensors are moved with 16-byte vector accesses.
+bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool al16(const void* a, const void* b, const void* c = nullptr, const void* d = nullptr,
+          const void* e = nullptr, const void* f = nullptr, const void* g = nullptr) {
+  return al16(a) && al16(b) && al16(c) && al16(d) && al16(e) && al16(f) && al16(g);
+}
+
 int hip_status(hipError_t e) {
   if (e == hipSuccess) return MOE_OK;
   (void)hipGetLastError();
@@ -463,6 +470,7 @@ int moe_route(const moe_config* c, int64_t T, const void* hidden, const void* ga
   MOE_TRY(check_T(c, T));
   if (!topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
   if (!scores_in && (!hidden || !gate_w)) return MOE_ERR_INVALID_ARG;
+  if (!scores_in && !al16(hidden, gate_w)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   RouteWs w{};
   // Without scores_out the logits need the workspace; with scores_out a
@@ -507,6 +515,7 @@ int moe_grouped_swiglu(const moe_config* c, int64_t T, const void* hidden, const
   if (hidden_scales && !is_fp8(c)) return MOE_ERR_INVALID_ARG;
   if (epilogue == MOE_EPI_STORE_ROWS && !expert_out) return MOE_ERR_INVALID_ARG;
   if (epilogue == MOE_EPI_SCATTER_ADD && (!acc || !topk_w || !inv_perm)) return MOE_ERR_INVALID_ARG;
+  if (!al16(hidden, w13, w2, expert_out, acc)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   const int64_t rows = T * c->top_k;
   const bool scatter = epilogue == MOE_EPI_SCATTER_ADD;
@@ -526,6 +535,7 @@ int moe_combine(const moe_config* c, int64_t T, const void* expert_out, const fl
   MOE_TRY(check_T(c, T));
   if (!out) return MOE_ERR_INVALID_ARG;
   if (expert_out && (!inv_perm || !topk_w)) return MOE_ERR_INVALID_ARG;
+  if (!al16(expert_out, acc, shared_out, out)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   HIP_TRY(launch_combine(act_dt(c), (int)T, c->hidden, c->top_k, expert_out, acc, inv_perm, topk_w, shared_out,
                          out, stream));
@@ -542,6 +552,7 @@ int moe_forward(const moe_config* c, int64_t T, const void* hidden, const void* 
   if (is_fp8(c) && (!w13_scales || !w2_scales)) return MOE_ERR_INVALID_ARG;
   if (c->shared_inter > 0 && (!sh_w13 || !sh_w2)) return MOE_ERR_INVALID_ARG;
   if (c->shared_inter > 0 && is_fp8(c) && (!sh_w13_scales || !sh_w2_scales)) return MOE_ERR_INVALID_ARG;
+  if (!al16(hidden, gate_w, w13, w2, sh_w13, sh_w2, out)) return MOE_ERR_INVALID_ARG;
   const int epi = opts ? opts->epilogue : MOE_EPI_STORE_ROWS;
   if (epi != MOE_EPI_STORE_ROWS && epi != MOE_EPI_SCATTER_ADD) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
@@ -618,6 +629,7 @@ int moe_quantize_fp8_1x128(int64_t rows, int64_t cols, const void* in, int32_t i
   if (in_dtype != MOE_F32 && in_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (rows == 0 || cols == 0) return MOE_OK;
   if (!in || !codes || !scales) return MOE_ERR_INVALID_ARG;
+  if (!al16(in) || ((uintptr_t)codes & 7u)) return MOE_ERR_INVALID_ARG;
   HIP_TRY(launch_quantize(in_dtype == MOE_F32 ? MOE_DT_F32 : MOE_DT_BF16, rows, cols, in, codes, scales, stream));
   return MOE_OK;
 }

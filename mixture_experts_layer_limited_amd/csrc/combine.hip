@@ -7,8 +7,38 @@
 
 namespace moe {
 
-// out[t] = acc[t] + sum_j w[t,j] * rows[inv[t*k+j]] + shared[t], fp32 sum,
-// one rounding.  One block per token, 8 columns per thread per step.
+// out[t] = acc[t] + sum_j w[t,j] * rows[inv[t*k+j]] + shared[t], fp32 sum in
+// that order, one rounding.  One block per token, 8 consecutive columns per
+// thread per pass, moved with 16-byte loads and stores (H % 8 == 0; row starts
+// are 16-byte aligned for every H the ABI accepts).
+template <int ADT>
+__device__ __forceinline__ void load8(const typename Elem<ADT>::T* p, float v[8]) {
+  if constexpr (ADT == MOE_DT_BF16) {
+    const u32x4 w = *(const u32x4*)p;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = __uint_as_float(w[q] << 16);
+      v[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+    }
+  } else {
+    const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+template <int ADT>
+__device__ __forceinline__ void store8(typename Elem<ADT>::T* p, const float v[8]) {
+  if constexpr (ADT == MOE_DT_BF16) {
+    u32x4 w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = f32_to_bf16_bits(v[2 * q]) | (f32_to_bf16_bits(v[2 * q + 1]) << 16);
+    *(u32x4*)p = w;
+  } else {
+    *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+    *(float4*)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
 template <int ADT>
 __global__ __launch_bounds__(256) void combine_kernel(int H, int k, const void* __restrict__ expert_out,
                                                       const float* __restrict__ acc,
@@ -29,28 +59,31 @@ __global__ __launch_bounds__(256) void combine_kernel(int H, int k, const void* 
   T* o = (T*)out;
   for (int c = threadIdx.x * 8; c < H; c += blockDim.x * 8) {
     float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
     if (acc) {
       const float4 a0 = *(const float4*)(acc + (int64_t)t * H + c);
       const float4 a1 = *(const float4*)(acc + (int64_t)t * H + c + 4);
       v[0] = a0.x; v[1] = a0.y; v[2] = a0.z; v[3] = a0.w;
       v[4] = a1.x; v[5] = a1.y; v[6] = a1.z; v[7] = a1.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
     }
     if (rows) {
       for (int j = 0; j < k; ++j) {
+        float r[8];
+        load8<ADT>(rows + (int64_t)pos[j] * H + c, r);
         const float w = wt[j];
-        const int64_t base = (int64_t)pos[j] * H + c;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] += w * Elem<ADT>::load(rows, base + i);
+        for (int i = 0; i < 8; ++i) v[i] += w * r[i];
       }
     }
     if (sh) {
+      float r[8];
+      load8<ADT>(sh + (int64_t)t * H + c, r);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] += Elem<ADT>::load(sh, (int64_t)t * H + c + i);
+      for (int i = 0; i < 8; ++i) v[i] += r[i];
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) Elem<ADT>::store(o, (int64_t)t * H + c + i, v[i]);
+    store8<ADT>(o + (int64_t)t * H + c, v);
   }
 }
 

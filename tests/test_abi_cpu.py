@@ -132,6 +132,10 @@ def test_entry_points_reject_before_launch():
     assert L.moe_load_balance(b(c), p, p, ctypes.c_float(float("nan")), p, null) == -1
     assert L.moe_load_balance(b(bad), p, p, ctypes.c_float(0.01), p, null) == -2
     assert L.moe_load_balance(b(c), p, null, ctypes.c_float(0.01), null, null) == 0   # nothing to do
+    q = ctypes.c_void_p(0x1008)         # 8- but not 16-byte aligned
+    assert L.moe_combine(b(c), 16, null, null, null, null, null, q, null) == -1     # misaligned out
+    assert L.moe_quantize_fp8_1x128(4, 128, q, 1, p, p, null) == -1               # misaligned input
+    assert L.moe_quantize_fp8_1x128(4, 128, p, 1, ctypes.c_void_p(0x1004), p, null) == -1
     assert L.moe_quantize_fp8_1x128(4, 100, p, 1, p, p, null) == -1
     assert L.moe_quantize_fp8_1x128(4, 128, p, 2, p, p, null) == -1
 
