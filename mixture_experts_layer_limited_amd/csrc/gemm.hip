@@ -15,6 +15,7 @@
 // count and surplus work-groups exit at once.
 #include "common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace moe {
 
@@ -264,11 +265,9 @@ static hipError_t launch_cfg(const GemmParams& p, int grid_m, hipStream_t s) {
   constexpr int BM = WM * TM * 32;
   constexpr int lds_bytes = 2 * (BM + BN) * 128;
   auto kern = gemm_kernel<DT, WM, WN, TM, TN, EPI, ODT>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+  {
+    const hipError_t e = allow_lds<gemm_kernel<DT, WM, WN, TM, TN, EPI, ODT>>(lds_bytes);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int64_t grid = (int64_t)grid_m * p.ntn;
   if (grid <= 0) return hipSuccess;

@@ -526,11 +526,9 @@ static hipError_t launch8_split(const GemmFp8Params& p, int grid_m, hipStream_t 
   constexpr int lds_bytes = SA * (BM * 128 + WM * WN * 256) + SB * BN * 128;
   static_assert(lds_bytes <= 160 * 1024, "LDS");
   auto kern = gemm_fp8_split_kernel<WM, WN, TM, TN, SA, SB, EPI>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+  {
+    const hipError_t e = allow_lds<gemm_fp8_split_kernel<WM, WN, TM, TN, SA, SB, EPI>>(lds_bytes);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int64_t grid = (int64_t)grid_m * p.ntn;
   if (grid <= 0) return hipSuccess;
@@ -561,11 +559,9 @@ static hipError_t launch8(const GemmFp8Params& p, int grid_m, hipStream_t s) {
   constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
   constexpr int lds_bytes = 2 * (BM + BN) * 128 + 2 * BM * 4;
   auto kern = gemm_fp8_kernel<WM, WN, TM, TN, EPI>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+  {
+    const hipError_t e = allow_lds<gemm_fp8_kernel<WM, WN, TM, TN, EPI>>(lds_bytes);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int64_t grid = (int64_t)grid_m * p.ntn;
   if (grid <= 0) return hipSuccess;

@@ -527,11 +527,9 @@ static hipError_t launch_split(const GemmParams& p, int grid_m, hipStream_t s) {
   constexpr int lds_bytes = (SA * BM + SB * BN) * 128;
   static_assert(lds_bytes <= 160 * 1024, "LDS");
   auto kern = gemm_split_kernel<WM, WN, TM, TN, SA, SB, EPI, ODT>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+  {
+    const hipError_t e = allow_lds<gemm_split_kernel<WM, WN, TM, TN, SA, SB, EPI, ODT>>(lds_bytes);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int64_t grid = (int64_t)grid_m * p.ntn;
   if (grid <= 0) return hipSuccess;
@@ -545,11 +543,9 @@ static hipError_t launch_pipe(const GemmParams& p, int grid_m, hipStream_t s) {
   constexpr int lds_bytes = S * (BM + BN) * ROWB;
   static_assert(lds_bytes * OCC <= 160 * 1024, "LDS");
   auto kern = gemm_pipe_kernel<TM, TN, S, OCC, ROWB, EPI, ODT>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+  {
+    const hipError_t e = allow_lds<gemm_pipe_kernel<TM, TN, S, OCC, ROWB, EPI, ODT>>(lds_bytes);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int64_t grid = (int64_t)grid_m * p.ntn;
   if (grid <= 0) return hipSuccess;

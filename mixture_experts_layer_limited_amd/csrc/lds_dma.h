@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace moe {
 
 typedef __attribute__((address_space(3))) char lds_char;
@@ -58,6 +60,21 @@ __device__ __forceinline__ void sub_schedule() {
   } else if constexpr (RS > MS) {
     __builtin_amdgcn_sched_group_barrier(0x100, RS - MS, 0);
   }
+}
+
+// Host side: opt kernel Kern into `bytes` of dynamic LDS, once per device (the
+// attribute is kept per device; 64 devices at most are remembered).
+template <auto Kern>
+hipError_t allow_lds(int bytes) {
+  static std::atomic<uint64_t> done{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (1ull << dev) : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute((const void*)Kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
 }
 
 }  // namespace moe
