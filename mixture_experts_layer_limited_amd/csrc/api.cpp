@@ -155,6 +155,7 @@ struct SwigluWs {
   void* h;                    // intermediate, act dtype (bf16 for FP8 weights)
   uint8_t* hq; float* h_scales; // FP8: E4M3 intermediate + 1x128 scales
   uint8_t* xq; float* xs;
+  float* xs_t;                // FP8: activation scales of the permuted rows, k-block-major
   float* row_w;
 };
 void carve_swiglu(Carver& cv, const moe_config* c, int64_t T, int64_t rows, int groups, int I,
@@ -178,9 +179,10 @@ void carve_swiglu(Carver& cv, const moe_config* c, int64_t T, int64_t rows, int 
     } else {
       w.xq = nullptr; w.xs = nullptr;
     }
+    w.xs_t = g1.kind == 1 ? cv.take<float>((size_t)rows * (c->hidden / 128)) : nullptr;
   } else {
     w.h = cv.take<char>((size_t)rows * I * act_bytes(c));
-    w.hq = nullptr; w.h_scales = nullptr; w.xq = nullptr; w.xs = nullptr;
+    w.hq = nullptr; w.h_scales = nullptr; w.xq = nullptr; w.xs = nullptr; w.xs_t = nullptr;
   }
   w.row_w = scatter ? cv.take<float>((size_t)rows) : nullptr;
 }
@@ -329,6 +331,10 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
     }
     GemmFp8Params p{};
     p.A = xq; p.a_scales = xs; p.a_rows = src;
+    if (g1.kind == 1) {  // the pipelined kernel reads the scales k-block-major over permuted rows
+      HIP_TRY(launch_gather_scales_t(xs, src, rows, H / 128, w.xs_t, s));
+      p.a_scales = w.xs_t; p.as_stride = rows;
+    }
     p.B = (const uint8_t*)w13; p.b_scales = w13_s;
     p.b_gstride = (int64_t)2 * I * H; p.bs_gstride = (int64_t)(2 * I / 128) * (H / 128);
     if (sg) { p.B2 = (const uint8_t*)sg->w13; p.b2_scales = sg->w13_s; p.b2_group = sg->group; }
@@ -341,9 +347,10 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
     MOE_TRY(mark(0));
     HIP_TRY(launch_gemm_fp8(EPI_SWIGLU, p, g1, gm1, s));
     MOE_TRY(mark(1));
-    HIP_TRY(launch_quantize(MOE_DT_BF16, rows, I, w.h, w.hq, w.h_scales, s));
+    const int64_t hst = g2.kind == 1 ? rows : 0;  // k-block-major h scales for the pipelined kernel
+    HIP_TRY(launch_quantize(MOE_DT_BF16, rows, I, w.h, w.hq, w.h_scales, s, hst));
     GemmFp8Params q{};
-    q.A = w.hq; q.a_scales = w.h_scales; q.a_rows = nullptr;
+    q.A = w.hq; q.a_scales = w.h_scales; q.a_rows = nullptr; q.as_stride = hst;
     q.B = (const uint8_t*)w2; q.b_scales = w2_s;
     q.b_gstride = (int64_t)H * I; q.bs_gstride = (int64_t)(H / 128) * (I / 128);
     if (sg) { q.B2 = (const uint8_t*)sg->w2; q.b2_scales = sg->w2_s; q.b2_group = sg->group; }

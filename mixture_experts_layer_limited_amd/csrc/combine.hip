@@ -132,7 +132,8 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
 // scale = fp32(amax / 448) (1 if amax == 0), code = E4M3(fp32(v / scale)).
 template <int IDT>
 __global__ __launch_bounds__(256) void quantize_kernel(int64_t rows, int64_t cols, const void* __restrict__ in,
-                                                       uint8_t* __restrict__ codes, float* __restrict__ scales) {
+                                                       uint8_t* __restrict__ codes, float* __restrict__ scales,
+                                                       int64_t st_stride) {
   // 16 lanes per 1x128 tile, 8 consecutive values per lane: one 16-byte (bf16)
   // or two (fp32) loads and one 8-byte store of codes per lane.
   using T = typename Elem<IDT>::T;
@@ -169,20 +170,43 @@ __global__ __launch_bounds__(256) void quantize_kernel(int64_t rows, int64_t col
     hi |= f32_to_e4m3(v[q + 4] / scale) << (8 * q);
   }
   *(uint2*)(codes + base) = make_uint2(lo, hi);
-  if (sub == 0) scales[r * tiles_per_row + c0 / 128] = scale;
+  if (sub == 0) {
+    if (st_stride > 0) scales[(c0 / 128) * st_stride + r] = scale;  // k-block-major
+    else scales[r * tiles_per_row + c0 / 128] = scale;
+  }
+}
+
+// scales_t[kb * rows + p] = scales[src(p) * nkb + kb]: the activation scales of the
+// permuted rows, k-block-major, so a GEMM step reads the scales of a row tile as
+// one contiguous run.
+__global__ __launch_bounds__(256) void gather_scales_t_kernel(const float* __restrict__ scales,
+                                                              const int32_t* __restrict__ src, int64_t rows, int nkb,
+                                                              float* __restrict__ scales_t) {
+  const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (p >= rows) return;
+  const int64_t s = src ? src[p] : p;
+  for (int kb = 0; kb < nkb; ++kb) scales_t[(int64_t)kb * rows + p] = scales[s * nkb + kb];
+}
+
+hipError_t launch_gather_scales_t(const float* scales, const int32_t* src, int64_t rows, int nkb, float* scales_t,
+                                  hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_scales_t_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, scales, src,
+                     rows, nkb, scales_t);
+  return hipGetLastError();
 }
 
 hipError_t launch_quantize(int in_dt, int64_t rows, int64_t cols, const void* in, uint8_t* codes, float* scales,
-                           hipStream_t s) {
+                           hipStream_t s, int64_t scales_t_stride) {
   const int64_t tiles = rows * (cols / 128);
   if (tiles <= 0) return hipSuccess;
   const int64_t grid = (tiles + 15) / 16;
   if (in_dt == MOE_DT_BF16)
     hipLaunchKernelGGL(quantize_kernel<MOE_DT_BF16>, dim3((unsigned)grid), dim3(256), 0, s, rows, cols, in, codes,
-                       scales);
+                       scales, scales_t_stride);
   else
     hipLaunchKernelGGL(quantize_kernel<MOE_DT_F32>, dim3((unsigned)grid), dim3(256), 0, s, rows, cols, in, codes,
-                       scales);
+                       scales, scales_t_stride);
   return hipGetLastError();
 }
 

@@ -294,7 +294,10 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_fp8_split_kernel(GemmFp8
   const cfloat* SBg = (const cfloat*)(g2_ ? p.b2_scales : p.b_scales + (int64_t)grp * p.bs_gstride);
   const int b_nrows = (EPI == EPI_SWIGLU) ? 2 * p.N : p.N;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, p.a_nrows * krow);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.a_scales, p.a_nrows * nkb * 4);
+  // activation scales: k-block-major over permuted rows (one contiguous run per
+  // row tile and step), or row-major over source rows
+  const bool st = p.as_stride > 0;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.a_scales, (st ? p.as_stride : p.a_nrows) * nkb * 4);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bg, (int64_t)b_nrows * krow);
 
   const int lrow = lane / CPR, lslot = lane % CPR;
@@ -313,12 +316,17 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_fp8_split_kernel(GemmFp8
   {
     const int r = wave * RW + lane;  // lanes past RW fill the wave's spare scale words
     if (lane < RW && r < rows) {
-      const int src = p.a_rows ? p.a_rows[r0 + r] : r0 + r;
-      vos = (uint32_t)((int64_t)src * nkb * 4);
+      if (st) {
+        vos = (uint32_t)((int64_t)(r0 + r) * 4);
+      } else {
+        const int src = p.a_rows ? p.a_rows[r0 + r] : r0 + r;
+        vos = (uint32_t)((int64_t)src * nkb * 4);
+      }
     } else {
       vos = 0x40000000u;
     }
   }
+  const uint32_t sstep = st ? (uint32_t)(p.as_stride * 4) : 4u;  // scale bytes between K steps
 #pragma unroll
   for (int i = 0; i < BI; ++i) {
     const int r = (wave * BI + i) * RPI + lrow;
@@ -365,7 +373,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_fp8_split_kernel(GemmFp8
     _Pragma("unroll") for (int i = (lo_); i < (hi_); ++i)                              \
       dma16(ra, slot_ + (wave * AI + i) * 1024, voa[i], soff_);                        \
     if (scales_) {                                                                     \
-      const uint32_t so4_ = (kt_) < nk ? (uint32_t)(kt_) * 4 : 0x80000000u;            \
+      const uint32_t so4_ = (kt_) < nk ? (uint32_t)(kt_) * sstep : 0x80000000u;        \
       dma4(rs, slot_ + ADATA + wave * 256, vos, so4_);                                 \
     }                                                                                  \
   } while (0)

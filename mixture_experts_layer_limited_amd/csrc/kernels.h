@@ -54,7 +54,8 @@ hipError_t launch_build_tiles(const int32_t* offsets, int E, int bm, int ntn, in
 // 128x128 fp32 block scales.
 struct GemmFp8Params {
   const uint8_t* A;
-  const float* a_scales;  // [rowsA, K/128]
+  const float* a_scales;  // [rowsA, K/128], or k-block-major when as_stride > 0
+  int64_t as_stride;      // > 0: scale of permuted row p, k-block kb at a_scales[kb * as_stride + p]
   const int32_t* a_rows;
   const uint8_t* B;
   const float* b_scales;  // group g: b_scales + g * bs_gstride, [Nrows/128, K/128]
@@ -106,7 +107,11 @@ hipError_t launch_combine(int adt, int T, int H, int k, const void* expert_out, 
                           hipStream_t s);
 hipError_t launch_load_balance(const int32_t* offsets, int E, float* bias, float gamma, ::moe_load_stats* stats,
                                hipStream_t s);
+// scales [rows, cols/128], or k-block-major [cols/128, scales_t_stride] when scales_t_stride > 0
 hipError_t launch_quantize(int in_dt, int64_t rows, int64_t cols, const void* in, uint8_t* codes,
-                           float* scales, hipStream_t s);
+                           float* scales, hipStream_t s, int64_t scales_t_stride = 0);
+// scales_t[kb * rows + p] = scales[src(p) * nkb + kb], src(p) = src[p] or p
+hipError_t launch_gather_scales_t(const float* scales, const int32_t* src, int64_t rows, int nkb, float* scales_t,
+                                  hipStream_t s);
 
 }  // namespace moe
