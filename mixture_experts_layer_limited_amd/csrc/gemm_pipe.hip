@@ -445,32 +445,37 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_split_kernel(GemmParams 
 #undef MOE_SPLIT_ISSUE_B
 
   if constexpr (ODT == MOE_DT_BF16 && (EPI == EPI_STORE || EPI == EPI_SWIGLU)) {
-    // bf16 tile through LDS (the ring is idle now): 2-byte writes in MFMA layout,
-    // then 16-byte row-contiguous global stores.  Rows are padded by 16 bytes so
-    // the two half-waves (rows 4 apart) write disjoint banks.
+    // bf16 tile through LDS (the ring is idle now), then 16-byte row-contiguous
+    // global stores.  Lanes l and l^1 trade one value per row pair (DPP) so each
+    // lane writes two adjacent columns of one row as a dword: even lanes row r,
+    // columns c and c+1; odd lanes row r+1, columns c-1 and c.  Rows are padded
+    // by 16 bytes.
     constexpr int OC = EPI == EPI_SWIGLU ? BN / 2 : BN;  // output columns of the tile
     constexpr int RB = OC * 2 + 16;                      // LDS bytes per staged row
+    constexpr int JO = EPI == EPI_SWIGLU ? TN / 2 : TN;  // output column blocks per wave
     static_assert(BM * RB <= SA * ASLOT + SB * BSLOT, "staging fits the ring");
+    const bool odd = lr & 1;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       if (i >= tm_live) continue;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = (wm + WM * i) * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
-        char* rp = lds + row * RB;
-        if constexpr (EPI == EPI_SWIGLU) {
+      for (int jo = 0; jo < JO; ++jo) {
+        const int c = (EPI == EPI_SWIGLU ? wn * (TN / 2) + jo : bblock(jo)) * 32 + lr;
 #pragma unroll
-          for (int j = 0; j < TN / 2; ++j) {
-            const int c = (wn * (TN / 2) + j) * 32 + lr;
-            *(uint16_t*)(rp + 2 * c) = (uint16_t)f32_to_bf16_bits(silu_mul_p(acc[i][j][e], acc[i][j + TN / 2][e]));
+        for (int e = 0; e < 16; e += 2) {
+          float v0, v1;
+          if constexpr (EPI == EPI_SWIGLU) {
+            v0 = silu_mul_p(acc[i][jo][e], acc[i][jo + TN / 2][e]);
+            v1 = silu_mul_p(acc[i][jo][e + 1], acc[i][jo + TN / 2][e + 1]);
+          } else {
+            v0 = acc[i][jo][e];
+            v1 = acc[i][jo][e + 1];
           }
-        } else {
-#pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            const int c = bblock(j) * 32 + lr;
-            *(uint16_t*)(rp + 2 * c) = (uint16_t)f32_to_bf16_bits(acc[i][j][e]);
-          }
+          const float recv = swap_adjacent_lanes(odd ? v0 : v1);
+          const int row = (wm + WM * i) * 32 + 8 * (e >> 2) + 4 * hi + (e & 3) + (odd ? 1 : 0);
+          const int col = odd ? c - 1 : c;
+          *(uint32_t*)(lds + row * RB + 2 * col) = odd ? pack_bf16_rne(recv, v1) : pack_bf16_rne(v0, recv);
         }
       }
     }
