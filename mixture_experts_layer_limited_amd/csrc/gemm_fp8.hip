@@ -493,6 +493,52 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_fp8_split_kernel(GemmFp8
 #undef MOE_F8_ISSUE_A
 #undef MOE_F8_ISSUE_B
 
+  if constexpr (EPI == EPI_STORE || EPI == EPI_SWIGLU) {
+    // bf16 tile through LDS (the rings are idle now) and 16-byte row stores; lanes
+    // l and l^1 trade one value per row pair so each lane writes a dword of two
+    // adjacent columns (even lanes row r, columns c, c+1; odd lanes row r+1,
+    // columns c-1, c).  Rows are padded by 16 bytes.
+    constexpr int OC = EPI == EPI_SWIGLU ? BN / 2 : BN;
+    constexpr int RB = OC * 2 + 16;
+    constexpr int JO = EPI == EPI_SWIGLU ? TN / 2 : TN;
+    static_assert(BM * RB <= SA * ASLOT + SB * BSLOT, "staging fits the rings");
+    const bool odd = lr & 1;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if (i >= tm_live) continue;
+#pragma unroll
+      for (int jo = 0; jo < JO; ++jo) {
+        const int c = (EPI == EPI_SWIGLU ? wn * (TN / 2) + jo : bblock(jo)) * 32 + lr;
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+          float v0, v1;
+          if constexpr (EPI == EPI_SWIGLU) {
+            v0 = silu_mul8(acc[i][jo][e], acc[i][jo + TN / 2][e]);
+            v1 = silu_mul8(acc[i][jo][e + 1], acc[i][jo + TN / 2][e + 1]);
+          } else {
+            v0 = acc[i][jo][e];
+            v1 = acc[i][jo][e + 1];
+          }
+          const float recv = swap_adjacent_lanes(odd ? v0 : v1);
+          const int row = (wm + WM * i) * 32 + 8 * (e >> 2) + 4 * hi + (e & 3) + (odd ? 1 : 0);
+          const int col = odd ? c - 1 : c;
+          *(uint32_t*)(lds + row * RB + 2 * col) = odd ? pack_bf16_rne(recv, v1) : pack_bf16_rne(v0, recv);
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int CPRo = OC / 8;
+    const int c0 = nt * OC;
+    for (int q = tid; q < BM * CPRo; q += NW * 64) {
+      const int row = q / CPRo, ch = q % CPRo;
+      const int col = c0 + ch * 8;
+      if (row < rows && col < p.N)
+        *(u32x4*)((uint16_t*)p.C + (int64_t)(r0 + row) * p.N + col) = *(const u32x4*)(lds + row * RB + ch * 16);
+    }
+    return;
+  }
+
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     if (i >= tm_live) continue;
