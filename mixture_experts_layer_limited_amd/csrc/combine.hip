@@ -141,7 +141,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(int64_t rows, int64_t col
   const int64_t tiles_per_row = cols / 128;
   const int64_t tile = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   if (tile >= rows * tiles_per_row) return;
-  const int64_t r = tile / tiles_per_row, c0 = (tile % tiles_per_row) * 128;
+  // row-major scales: consecutive tiles along a row; k-block-major scales:
+  // consecutive tiles down a column of tiles, so the scale stores coalesce
+  const int64_t r = st_stride > 0 ? tile % rows : tile / tiles_per_row;
+  const int64_t c0 = (st_stride > 0 ? tile / rows : tile % tiles_per_row) * 128;
   const int64_t base = r * cols + c0 + 8 * sub;
   float v[8];
   if constexpr (IDT == MOE_DT_BF16) {
