@@ -213,6 +213,10 @@ SMALL = {
     # H and I not multiples of the 256-wide n-tiles; shared expert as one more group
     "odd_dims": _reduced("v3_prefill_bf16", tokens=333, hidden=576, inter=192, n_experts=16, n_group=4,
                          topk_group=2, top_k=4, shared_inter=192),
+    # the largest expert count and top-k the library takes (1024, 32): many empty
+    # experts, 1024 groups in the tile builder, 32 rows per token in the combine
+    "max_experts_top_k": _reduced("v3_prefill_bf16", tokens=150, hidden=256, inter=128, n_experts=1024,
+                                  top_k=32, shared_inter=128),
     # shared expert of the routed width at T > 1024: its own dense launches
     "wide_shared_large_t": _reduced("v3_prefill_bf16", tokens=1100, hidden=512, inter=256, n_experts=32,
                                     shared_inter=256),
