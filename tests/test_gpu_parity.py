@@ -456,3 +456,38 @@ def test_forward_is_deterministic(name):
         outs.append(out)
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("name", ["v3_small", "fp8_small"])
+def test_forward_in_a_hip_graph(name):
+    """moe_forward allocates nothing and never synchronises, so a whole layer can
+    be captured into a HIP graph: every replay, with eager work in between,
+    equals the eager forward."""
+    cfg = SMALL[name]
+    inp = layer_inputs(cfg, 5, DEV)
+    c = binding_config(cfg)
+    T, H = cfg.tokens, cfg.hidden
+    ws = moe.workspace(c, T)
+    args = (inp["x"], inp["gate_w"], inp["bias"], inp["w13"], inp["w13_s"], inp["w2"], inp["w2_s"],
+            inp["sh_w13"], inp["sh_w13_s"], inp["sh_w2"], inp["sh_w2_s"])
+    ref = torch.empty(T, H, dtype=inp["x"].dtype, device=DEV)
+    moe.forward(c, T, *args, ref, ws)
+    torch.cuda.synchronize()
+    out = torch.empty_like(ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                      # warm-up on the capture stream
+        moe.forward(c, T, *args, out, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.forward(c, T, *args, out, ws)
+    for rep in range(3):
+        out.zero_()
+        noise = torch.randn(1 << 20, device=DEV).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {rep} differs from the eager forward"
+        del noise
