@@ -23,6 +23,12 @@ Distributions:
     weight_block_size [128, 128]); the conversion is done here, offline,
     with torch's float8_e4m3fn cast: it is part of preparing the weights,
     not part of the layer.
+  * W4A16 workloads store expert weights as signed 4-bit integers, two per
+    byte (even input column in the low nibble), with one fp32 scale per
+    output row and 128 input columns (walkthrough §8 quantisation table
+    names the format; the packing and grouping are this library's reading).
+    The conversion is done here, offline: symmetric, scale = amax / 7 (1 for
+    an all-zero group), q = round-half-even(w / scale), clamped to [-8, 7].
 
 Routing inputs (x, gate weight, bias) are always drawn on the CPU so that
 they are identical wherever the layer runs; expert weights are drawn on the
@@ -61,7 +67,7 @@ class LayerConfig:
     scoring: str         # "softmax" | "sigmoid"
     norm_topk_prob: bool
     routed_scaling_factor: float
-    dtype: str           # "f32" | "bf16" | "fp8"
+    dtype: str           # "f32" | "bf16" | "fp8" | "w4a16"
     bias: str            # "none" | "zero" | "zipf"
     outlier_frac: float = 0.0
     outlier_scale: float = 1.0
@@ -105,6 +111,11 @@ PRESETS: Dict[str, LayerConfig] = {
         n_group=8, topk_group=4, shared_inter=2048, scoring="sigmoid",
         norm_topk_prob=True, routed_scaling_factor=2.5, dtype="fp8", bias="zero",
         outlier_frac=1e-3, outlier_scale=20.0),
+    # V3 decode batch with 4-bit expert weights and bf16 activations (walkthrough §8).
+    "v3_decode_w4a16": LayerConfig(
+        "v3_decode_w4a16", tokens=128, hidden=7168, inter=2048, n_experts=256, top_k=8,
+        n_group=8, topk_group=4, shared_inter=2048, scoring="sigmoid",
+        norm_topk_prob=True, routed_scaling_factor=2.5, dtype="w4a16", bias="zipf"),
 }
 
 
@@ -171,10 +182,33 @@ def fp8_block_quantize(w: torch.Tensor):
     return codes.contiguous(), scale.contiguous()
 
 
+def int4_group_quantize(w: torch.Tensor):
+    """Packed signed 4-bit codes (n, k/2) uint8 and fp32 scales (n, k/128) of a
+    2-D fp32 weight: one symmetric scale per row and 128 columns."""
+    n, k = w.shape
+    if k % 128:
+        raise ValueError("4-bit weights need a multiple of 128 input columns")
+    g = w.reshape(n, k // 128, 128)
+    amax = g.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / 7.0, torch.ones_like(amax))
+    q = torch.round(g / scale[:, :, None]).clamp_(-8, 7).to(torch.int16).reshape(n, k)
+    nib = q & 0xF
+    packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).to(torch.uint8)
+    return packed.contiguous(), scale.contiguous()
+
+
 def _stacked(cfg: LayerConfig, name: str, n_out: int, n_in: int, count: int, seed: int,
              device, fp8: bool):
     """count matrices (n_out, n_in) ~ N(0, 1/n_in), one generator per matrix."""
     std = n_in ** -0.5
+    if cfg.dtype == "w4a16":
+        codes = torch.empty(count, n_out, n_in // 2, dtype=torch.uint8, device=device)
+        scales = torch.empty(count, n_out, n_in // 128, dtype=torch.float32, device=device)
+        for e in range(count):
+            c, s = int4_group_quantize(_normal((n_out, n_in), std, seed, name, e, device))
+            codes[e].copy_(c)
+            scales[e].copy_(s)
+        return codes, scales
     if fp8:
         codes = torch.empty(count, n_out, n_in, dtype=torch.uint8, device=device)
         scales = torch.empty(count, n_out // 128, n_in // 128, dtype=torch.float32, device=device)
@@ -193,7 +227,9 @@ def expert_weights(cfg: LayerConfig, seed: int = 0, device="cpu") -> Dict[str, O
     """Stacked routed weights w13 (E,2I,H), w2 (E,H,I) and the shared expert's
     gate_up (2Is,H) / down (H,Is), all (out,in).  Gate rows are [0,I) of w13 and
     up rows [I,2I) (walkthrough §2.2, §3.3.1).  FP8 configs also return block
-    scales w13_s (E,2I/128,H/128), w2_s (E,H/128,I/128), sh_w13_s, sh_w2_s."""
+    scales w13_s (E,2I/128,H/128), w2_s (E,H/128,I/128), sh_w13_s, sh_w2_s.
+    W4A16 configs return packed codes w13 (E,2I,H/2), w2 (E,H,I/2) and group
+    scales w13_s (E,2I,H/128), w2_s (E,H,I/128) (shared: without the E axis)."""
     fp8 = cfg.dtype == "fp8"
     E, H, I, Is = cfg.n_experts, cfg.hidden, cfg.inter, cfg.shared_inter
     w13, w13_s = _stacked(cfg, "w13", 2 * I, H, E, seed, device, fp8)

@@ -14,10 +14,11 @@ Everything here is written from the pages' statement of the layer:
   * DeepSeek V3/R1 overview, xxqk.cn/news/389306 (§2.2 bias-based
     load balancing);
   * MoA routing + FP8 inference, blog.hotdry.top (FP8 section: E4M3,
-    1x128 activation tiles, 128x128 weight blocks).
+    1x128 activation tiles, 128x128 weight blocks);
+  * the walkthrough's §8 quantisation table (4-bit W4A16 expert weights).
 
 Pins (what checks the oracle against something other than itself) live in
-tests/test_oracle_*.py.  Every function in moe.py and e4m3.py is pinned;
+tests/test_oracle_*.py.  Every function in moe.py, e4m3.py and int4.py is pinned;
 none is "parity unpinned".
 """
 from .moe import (  # noqa: F401
@@ -28,4 +29,7 @@ from .moe import (  # noqa: F401
 from .e4m3 import (  # noqa: F401
     E4M3_MAX, e4m3_decode, e4m3_encode, quantize_1x128, dequantize_1x128,
     dequantize_blocks,
+)
+from .int4 import (  # noqa: F401
+    INT4_GROUP, int4_decode, unpack_int4, dequantize_int4_groups,
 )

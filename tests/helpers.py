@@ -9,7 +9,7 @@ import torch
 import oracle
 from moe_inputs import LayerConfig
 
-TOL = {"f32": 1e-4, "bf16": 1e-2, "fp8": 3e-2}
+TOL = {"f32": 1e-4, "bf16": 1e-2, "fp8": 3e-2, "w4a16": 1e-2}
 
 
 def f64(t: torch.Tensor) -> np.ndarray:
@@ -35,19 +35,22 @@ def binding_config(cfg: LayerConfig):
 
 class ExpertSource:
     """Per-expert fp64 weights for the oracle, decoded one expert at a time
-    from the tensors the GPU received (bf16/fp32 values, or E4M3 codes with
-    128x128 block scales)."""
+    from the tensors the GPU received (bf16/fp32 values, E4M3 codes with
+    128x128 block scales, or packed 4-bit codes with per-row 128-column
+    group scales)."""
 
-    def __init__(self, inp: dict, fp8: bool):
-        self.inp, self.fp8 = inp, fp8
+    def __init__(self, inp: dict, dtype: str):
+        self.inp, self.dtype = inp, dtype
         self.cache = {}
 
     def _w(self, name, e=None):
         t = self.inp[name] if e is None else self.inp[name][e]
-        if not self.fp8:
+        if self.dtype not in ("fp8", "w4a16"):
             return f64(t)
         s = self.inp[name + "_s"] if e is None else self.inp[name + "_s"][e]
-        return oracle.dequantize_blocks(u8(t), s.float().cpu().numpy())
+        if self.dtype == "fp8":
+            return oracle.dequantize_blocks(u8(t), s.float().cpu().numpy())
+        return oracle.dequantize_int4_groups(u8(t), s.float().cpu().numpy())
 
     def expert(self, e: int):
         if e not in self.cache:
@@ -81,7 +84,7 @@ def oracle_routing(cfg: LayerConfig, gpu_scores: np.ndarray, bias):
 
 
 def oracle_forward_rows(cfg: LayerConfig, inp: dict, ids, w, tokens):
-    src = ExpertSource(inp, cfg.dtype == "fp8")
+    src = ExpertSource(inp, cfg.dtype)
     qx, qh = fp8_quantizers(cfg)
     return oracle.moe_layer_rows(tokens, f64(inp["x"]), ids, w, src.expert, src.shared, quantize_x=qx,
                                  quantize_h=qh)

@@ -291,7 +291,7 @@ def test_grouped_swiglu_skewed(mode):
     moe.grouped_swiglu(c, T, inp["x"], None, dev(src), dev(off), inp["w13"], None, inp["w2"], None,
                        moe.MOE_EPI_STORE_ROWS, None, None, rows, None, ws)
     torch.cuda.synchronize()
-    srcx = ExpertSource(inp, False)
+    srcx = ExpertSource(inp, "bf16")
     ref = oracle.expert_outputs(f64(inp["x"]), off, src, srcx.expert)
     err = rel_err(f64(rows), ref)
     say(f"  max rel err {err:.3e}")
