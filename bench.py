@@ -24,7 +24,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "fp8": 5000.0}   # MI355X dense MFMA (fp32: vector/matrix fp32)
+# MI355X dense MFMA (fp32: vector/matrix fp32); 4-bit weights are widened to bf16 for the MFMAs
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "fp8": 5000.0, "w4a16": 2500.0}
 PEAK_HBM_GBS = 8000.0
 METRIC = "MoE layer tokens/s + grouped-GEMM TFLOPS (% MFMA peak) at V3 shape, 1 GPU"
 
@@ -100,8 +101,8 @@ def cpu_baseline(cfg, inp, n_tokens):
     """The fp64 oracle, as it stands, on the first n_tokens tokens of the batch:
     fp64 router GEMM + scoring + group-limited top-k for those tokens, then
     their expert FFNs and the shared expert with weights decoded from the
-    stored bf16/E4M3 values.  Weights of the experts the sample needs are
-    copied to host memory first (not timed)."""
+    stored bf16 / E4M3 / 4-bit values.  Weights of the experts the sample
+    needs are copied to host memory first (not timed)."""
     import numpy as np
     import oracle
     from threadpoolctl import threadpool_info
@@ -114,21 +115,24 @@ def cpu_baseline(cfg, inp, n_tokens):
                              routed_scaling_factor=cfg.routed_scaling_factor)
     need = sorted({int(e) for e in ids.reshape(-1)})
     fp8 = cfg.dtype == "fp8"
-    host = {e: tuple(inp[n][e].cpu() for n in (("w13", "w13_s", "w2", "w2_s") if fp8 else ("w13", "w2")))
+    scaled = cfg.dtype in ("fp8", "w4a16")
+    host = {e: tuple(inp[n][e].cpu() for n in (("w13", "w13_s", "w2", "w2_s") if scaled else ("w13", "w2")))
             for e in need}
-    sh = tuple(inp[n].cpu() for n in (("sh_w13", "sh_w13_s", "sh_w2", "sh_w2_s") if fp8 else ("sh_w13", "sh_w2")))
+    sh = tuple(inp[n].cpu() for n in (("sh_w13", "sh_w13_s", "sh_w2", "sh_w2_s") if scaled else ("sh_w13", "sh_w2")))
 
     def dec(t, sc=None):
         if sc is None:
             return t.float().double().numpy()
-        return oracle.dequantize_blocks(t.numpy(), sc.numpy())
+        if fp8:
+            return oracle.dequantize_blocks(t.numpy(), sc.numpy())
+        return oracle.dequantize_int4_groups(t.numpy(), sc.numpy())
 
     def get_expert(e):
         h = host[e]
-        return (dec(h[0], h[1]), dec(h[2], h[3])) if fp8 else (dec(h[0]), dec(h[1]))
+        return (dec(h[0], h[1]), dec(h[2], h[3])) if scaled else (dec(h[0]), dec(h[1]))
 
     def get_shared():
-        return (dec(sh[0], sh[1]), dec(sh[2], sh[3])) if fp8 else (dec(sh[0]), dec(sh[1]))
+        return (dec(sh[0], sh[1]), dec(sh[2], sh[3])) if scaled else (dec(sh[0]), dec(sh[1]))
 
     q = None
     if fp8:
@@ -200,7 +204,7 @@ def main():
     g2 = float(np.mean([ev.ms(ev.ev[4 * i + 2], ev.ev[4 * i + 3]) for i in range(a.steps)]))
     ev.close()
 
-    eb = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.dtype]
+    eb = {"f32": 4, "bf16": 2, "fp8": 1, "w4a16": 0.5}[cfg.dtype]   # bytes per expert weight
     ab = 4 if cfg.dtype == "f32" else 2
     # With the routed experts' width, stored rows and T <= 1024, the shared expert runs
     # as one more group of the routed GEMM launches, so the timed grouped GEMMs include it.
@@ -215,6 +219,9 @@ def main():
     if cfg.dtype == "fp8":
         bytes1 += groups * (2 * I // 128) * (H // 128) * 4 + T * (H // 128) * 4
         bytes2 += groups * (H // 128) * (I // 128) * 4
+    if cfg.dtype == "w4a16":  # one fp32 scale per weight row and 128 columns
+        bytes1 += groups * (2 * I) * (H // 128) * 4
+        bytes2 += groups * H * (I // 128) * 4
     peak = PEAK_TFLOPS[cfg.dtype]
     ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
     intensity = flops1 / bytes1
@@ -241,11 +248,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.dtype,
+        "dtype": "bf16" if cfg.dtype == "w4a16" else cfg.dtype,
         "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
         "config": {"workload": f"{cfg.name}: T={T} H={H} E={E} I={I} k={k} groups {cfg.n_group}/{cfg.topk_group} "
                                f"{cfg.scoring} shared Is={Is}", "tokens": T, "hidden": H, "experts": E,
                    "inter": I, "top_k": k, "shared_inter": Is, "epilogue": a.epilogue,
+                   "expert_weights": {"f32": "fp32", "bf16": "bf16", "fp8": "E4M3 + 128x128 fp32 scales",
+                                      "w4a16": "int4 + fp32 scale per row and 128 columns"}[cfg.dtype],
                    "non_empty_experts": non_empty},
         "grouped_gemm": {"ms_gate_up": g1, "ms_down": g2, "shared_expert_included": merged,
                          "tflops": gg_tflops, "peak_tflops": peak,

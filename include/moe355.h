@@ -23,7 +23,9 @@
  *     gate projection (w1) in rows [0,I) and the up projection (w3) in rows
  *     [I,2I); w2 (E,H,I); shared gate_up (2Is,H) split the same way; shared
  *     down (H,Is) (walkthrough §2.2-§2.3 stacked storage, §3.3 x @ w.T);
- *   - index tensors are int32; T*k < 2^31;
+ *   - index tensors are int32; T*k < 2^31; the hidden rows (T*H elements) and
+ *     the intermediate rows ((T*k + T) * max(I, Is) elements) span less than
+ *     2^31 bytes in the activation dtype (MOE_ERR_UNSUPPORTED otherwise);
  *   - activation, weight and output tensors (hidden, gate_w, w13, w2, sh_w13,
  *     sh_w2, expert_out, acc, shared_out, out, quantiser input) start on a
  *     16-byte boundary, E4M3 code outputs on an 8-byte boundary, every other
@@ -61,7 +63,12 @@ typedef enum {
 
 typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_scoring;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+/* MOE_INT4: signed 4-bit expert weights (walkthrough §8 quantisation table,
+ * W4A16), two's complement in [-8, 7], two per byte: input column 2j in the
+ * low nibble (bits 0-3) of byte j of its row, column 2j+1 in the high nibble;
+ * a weight matrix stored (out, in) is (out, in/2) bytes, with one fp32 scale
+ * per output row and 128 input columns, (out, in/128); value = q * scale. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_INT4 = 3 } moe_dtype;
 
 typedef enum { MOE_EPI_STORE_ROWS = 0, MOE_EPI_SCATTER_ADD = 1 } moe_epilogue;
 
@@ -76,7 +83,8 @@ typedef enum {
 /*
  * Layer configuration (walkthrough §1.3 MoE config keys; V3 lab page §3
  * moe_router.json).
- *   hidden, inter        H and I; multiples of 64 (of 128 for FP8 weights)
+ *   hidden, inter        H and I; multiples of 64 (of 128 for FP8 and
+ *                        4-bit weights)
  *   n_experts            E, 1..1024
  *   top_k                k, 1..min(E, 32)
  *   n_group, topk_group  E % n_group == 0; 1 <= topk_group <= n_group; when
@@ -84,7 +92,8 @@ typedef enum {
  *                        k <= topk_group * E / n_group.  n_group == 1 is plain
  *                        (greedy) top-k.
  *   shared_inter         Is = n_shared * shared expert intermediate size;
- *                        0 = no shared expert; multiple of 64 (128 for FP8)
+ *                        0 = no shared expert; multiple of 64 (128 for FP8
+ *                        and 4-bit weights)
  *   scoring              moe_scoring
  *   norm_topk_prob       0/1: divide the k weights by their sum
  *   routed_scaling_factor  multiplies every routing weight
@@ -94,7 +103,11 @@ typedef enum {
  *                        act_dtype, or MOE_FP8_E4M3 with act_dtype MOE_BF16
  *                        (E4M3 codes + one fp32 scale per 128x128 block;
  *                        activations are then quantised to E4M3 per 1x128 tile
- *                        inside the layer; the router stays in bf16)
+ *                        inside the layer; the router stays in bf16), or
+ *                        MOE_INT4 with act_dtype MOE_BF16 (4-bit codes + one
+ *                        fp32 scale per weight row and 128 input columns;
+ *                        activations stay bf16, the intermediate is rounded
+ *                        to bf16; the router stays in bf16)
  *   out_dtype            must equal act_dtype
  */
 typedef struct moe_config {
@@ -189,13 +202,18 @@ int moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_ids,
  *   x_p = hidden[permuted_src[p]]   (permuted_src == NULL: x_p = hidden[p])
  *   y_p = (SiLU(x_p w13[e][0:I]^T) * (x_p w13[e][I:2I]^T)) w2[e]^T
  * in fp32 accumulation, SiLU and product in fp32, the intermediate rounded to
- * the activation dtype (bf16, or E4M3 with 1x128 scales for FP8 weights).
+ * the activation dtype (bf16, or E4M3 with 1x128 scales for FP8 weights;
+ * bf16 for 4-bit weights, whose codes are applied exactly: each 128-column
+ * group's dot product is accumulated in fp32 and multiplied by its scale).
  *   hidden         [T,H] act_dtype, or E4M3 codes when hidden_scales != NULL
  *   hidden_scales  [T,H/128] fp32 1x128 scales of E4M3 codes, or NULL
  *   permuted_src, expert_offsets   as produced by moe_permute; the number of
  *                  rows is expert_offsets[E] <= T*k
  *   w13, w2        weight_dtype; w13_scales [E,2I/128,H/128] and
- *                  w2_scales [E,H/128,I/128] fp32 for FP8 weights, else NULL
+ *                  w2_scales [E,H/128,I/128] fp32 for FP8 weights;
+ *                  4-bit weights: w13 [E,2I,H/2] and w2 [E,H,I/2] bytes with
+ *                  w13_scales [E,2I,H/128] and w2_scales [E,H,I/128] fp32;
+ *                  NULL for bf16 / fp32 weights
  *   epilogue       MOE_EPI_STORE_ROWS: expert_out[p] = y_p, [T*k,H] act_dtype
  *                  MOE_EPI_SCATTER_ADD: acc[permuted_src[p]] += w_p * y_p with
  *                  w_p = topk_w[a] for the copy a with inv_perm[a] = p; acc is
@@ -232,7 +250,9 @@ int moe_combine(const moe_config* cfg, int64_t T, const void* expert_out, const 
  * experts and for the shared expert, moe_combine, all on `stream`.
  *   hidden [T,H], gate_w [E,H] act_dtype; bias [E] fp32 or NULL;
  *   w13, w2 (+ scales) as in moe_grouped_swiglu; sh_w13 [2Is,H], sh_w2 [H,Is]
- *   (+ scales [2Is/128,H/128], [H/128,Is/128] for FP8), NULL when Is == 0;
+ *   (+ scales [2Is/128,H/128], [H/128,Is/128] for FP8; packed [2Is,H/2],
+ *   [H,Is/2] with scales [2Is,H/128], [H,Is/128] for 4-bit weights), NULL
+ *   when Is == 0;
  *   out [T,H] act_dtype; opts may be NULL (store-rows epilogue, no extra
  *   outputs).
  */

@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # MOE355_LIB names another build of the same library (e.g. a tuning variant).
 LIB_PATH = os.environ.get("MOE355_LIB", os.path.join(_HERE, "libmoe355.so"))
 
-MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_INT4 = 0, 1, 2, 3
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_EPI_STORE_ROWS, MOE_EPI_SCATTER_ADD = 0, 1
 MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_GROUPED_SWIGLU, MOE_OP_COMBINE, MOE_OP_FORWARD = range(5)
@@ -55,10 +55,11 @@ class ForwardOpts(ctypes.Structure):
 def make_config(*, hidden, inter, n_experts, top_k, n_group=1, topk_group=1, shared_inter=0,
                 scoring="softmax", norm_topk_prob=False, routed_scaling_factor=1.0,
                 dtype="bf16") -> MoeConfig:
-    """dtype: "f32" (everything fp32), "bf16" (bf16 activations and weights) or
-    "fp8" (bf16 activations and router, E4M3 expert weights)."""
+    """dtype: "f32" (everything fp32), "bf16" (bf16 activations and weights),
+    "fp8" (bf16 activations and router, E4M3 expert weights) or "w4a16" (bf16
+    activations and router, 4-bit expert weights)."""
     act = MOE_F32 if dtype == "f32" else MOE_BF16
-    wdt = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}[dtype]
+    wdt = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "w4a16": MOE_INT4}[dtype]
     return MoeConfig(hidden, inter, n_experts, top_k, n_group, topk_group, shared_inter,
                      MOE_SCORE_SOFTMAX if scoring == "softmax" else MOE_SCORE_SIGMOID,
                      int(bool(norm_topk_prob)), float(routed_scaling_factor), act, wdt, act)

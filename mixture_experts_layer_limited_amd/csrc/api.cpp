@@ -31,6 +31,9 @@ struct Carver {
 };
 
 bool is_fp8(const moe_config* c) { return c->weight_dtype == MOE_FP8_E4M3; }
+bool is_w4(const moe_config* c) { return c->weight_dtype == MOE_INT4; }
+// weights that come with scale tensors
+bool has_scales(const moe_config* c) { return is_fp8(c) || is_w4(c); }
 int act_dt(const moe_config* c) { return c->act_dtype == MOE_F32 ? MOE_DT_F32 : MOE_DT_BF16; }
 size_t act_bytes(const moe_config* c) { return c->act_dtype == MOE_F32 ? 4 : 2; }
 
@@ -39,7 +42,8 @@ int check_cfg(const moe_config* c) {
   if (c->scoring != MOE_SCORE_SOFTMAX && c->scoring != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
   if (c->norm_topk_prob != 0 && c->norm_topk_prob != 1) return MOE_ERR_INVALID_ARG;
   if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
-  if (c->weight_dtype != MOE_F32 && c->weight_dtype != MOE_BF16 && c->weight_dtype != MOE_FP8_E4M3)
+  if (c->weight_dtype != MOE_F32 && c->weight_dtype != MOE_BF16 && c->weight_dtype != MOE_FP8_E4M3 &&
+      c->weight_dtype != MOE_INT4)
     return MOE_ERR_INVALID_ARG;
   if (c->out_dtype != MOE_F32 && c->out_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (c->hidden <= 0 || c->inter <= 0 || c->n_experts <= 0 || c->top_k <= 0 || c->n_group <= 0 ||
@@ -55,9 +59,8 @@ int check_cfg(const moe_config* c) {
   // Limits of this implementation.
   if (c->n_experts > 1024 || c->top_k > 32 || c->n_group > 64) return MOE_ERR_UNSUPPORTED;
   if (c->out_dtype != c->act_dtype) return MOE_ERR_UNSUPPORTED;
-  if (c->weight_dtype != c->act_dtype && !(c->weight_dtype == MOE_FP8_E4M3 && c->act_dtype == MOE_BF16))
-    return MOE_ERR_UNSUPPORTED;
-  const int mult = is_fp8(c) ? 128 : 64;
+  if (c->weight_dtype != c->act_dtype && !(has_scales(c) && c->act_dtype == MOE_BF16)) return MOE_ERR_UNSUPPORTED;
+  const int mult = has_scales(c) ? 128 : 64;
   if (c->hidden % mult || c->inter % mult || c->shared_inter % mult) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -66,6 +69,13 @@ int check_T(const moe_config* c, int64_t T) {
   if (T < 0) return MOE_ERR_INVALID_ARG;
   if (T * (int64_t)c->top_k >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
   if (T * (int64_t)c->n_experts >= (int64_t)1 << 40) return MOE_ERR_UNSUPPORTED;
+  // The GEMMs address their activation operands (hidden rows, the
+  // intermediate rows) with 32-bit buffer offsets.
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t eb = c->act_dtype == MOE_F32 ? 4 : 2;
+  const int64_t wide = c->shared_inter > c->inter ? c->shared_inter : c->inter;
+  if (T * c->hidden * eb >= lim) return MOE_ERR_UNSUPPORTED;
+  if ((T * c->top_k + T) * wide * eb >= lim) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -147,6 +157,17 @@ GemmShape fp8_shape2(const moe_config* c, int64_t rows, int groups, int I) {
   return gemm_fp8_shape((int)(rows / groups), rows * I, (int64_t)c->hidden * I);
 }
 
+GemmShape tile_shape1(const moe_config* c, int64_t T, int64_t rows, int groups, int I) {
+  if (is_fp8(c)) return fp8_shape1(c, T, rows, groups, I);
+  if (is_w4(c)) return gemm_w4_shape();
+  return shape1(c, T, rows, groups, I);
+}
+GemmShape tile_shape2(const moe_config* c, int64_t rows, int groups, int I) {
+  if (is_fp8(c)) return fp8_shape2(c, rows, groups, I);
+  if (is_w4(c)) return gemm_w4_shape();
+  return shape2(c, rows, groups, I);
+}
+
 // Workspace of one grouped SwiGLU over `rows` permuted rows of `groups` experts
 // with intermediate size I.
 struct SwigluWs {
@@ -162,8 +183,8 @@ void carve_swiglu(Carver& cv, const moe_config* c, int64_t T, int64_t rows, int 
                   bool quantize_x, bool scatter, SwigluWs& w) {
   const int64_t avg = rows / groups;
   (void)avg;
-  const GemmShape g1 = is_fp8(c) ? fp8_shape1(c, T, rows, groups, I) : shape1(c, T, rows, groups, I);
-  const GemmShape g2 = is_fp8(c) ? fp8_shape2(c, rows, groups, I) : shape2(c, rows, groups, I);
+  const GemmShape g1 = tile_shape1(c, T, rows, groups, I);
+  const GemmShape g2 = tile_shape2(c, rows, groups, I);
   // tile lists: every (m-tile, n-tile) pair of the gate/up and of the down GEMM
   w.tiles1 = cv.take<int4>((size_t)max_mtiles(rows, g1.bm, groups) * ntiles_n(I, g1.bn / 2) + 1);
   w.ntiles1 = cv.take<int>(1);
@@ -371,6 +392,48 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
     }
     return mark(3);
   }
+  if (is_w4(c)) {
+    const GemmShape g1 = gemm_w4_shape(), g2 = gemm_w4_shape();
+    const bool dense = offsets == nullptr;
+    const int ntn1 = ntiles_n(I, g1.bn / 2), ntn2 = ntiles_n(H, g2.bn);
+    if (!dense) {
+      HIP_TRY(launch_build_tiles(offsets, groups, g1.bm, ntn1, w.tiles1, w.ntiles1, s));
+      HIP_TRY(launch_build_tiles(offsets, groups, g2.bm, ntn2, w.tiles2, w.ntiles2, s));
+    }
+    GemmW4Params p{};
+    p.A = hidden; p.a_rows = src;
+    p.B = (const uint8_t*)w13; p.b_scales = w13_s;
+    p.b_gstride = (int64_t)2 * I * (H / 2); p.bs_gstride = (int64_t)2 * I * (H / 128);
+    if (sg) { p.B2 = (const uint8_t*)sg->w13; p.b2_scales = sg->w13_s; p.b2_group = sg->group; }
+    p.K = H; p.N = I; p.C = w.h;
+    p.a_nrows = T;
+    set_tiles(p, dense, rows, g1.bm, w.tiles1, w.ntiles1);
+    p.ntn = ntn1;
+    MOE_TRY(mark(0));
+    HIP_TRY(launch_gemm_w4(EPI_SWIGLU, MOE_DT_BF16, p, g1, dense ? p.n_mtiles : max_mtiles(rows, g1.bm, groups), s));
+    MOE_TRY(mark(1));
+    GemmW4Params q{};
+    q.A = w.h; q.a_rows = nullptr;
+    q.B = (const uint8_t*)w2; q.b_scales = w2_s;
+    q.b_gstride = (int64_t)H * (I / 2); q.bs_gstride = (int64_t)H * (I / 128);
+    if (sg) { q.B2 = (const uint8_t*)sg->w2; q.b2_scales = sg->w2_s; q.b2_group = sg->group; }
+    q.K = I; q.N = H;
+    q.a_nrows = rows;
+    set_tiles(q, dense, rows, g2.bm, w.tiles2, w.ntiles2);
+    q.ntn = ntn2;
+    const int gm2 = dense ? q.n_mtiles : max_mtiles(rows, g2.bm, groups);
+    if (epi == MOE_EPI_SCATTER_ADD) {
+      HIP_TRY(launch_row_weights(topk_w, inv, (int)rows, w.row_w, s));
+      q.C = acc; q.c_rows = src; q.row_w = w.row_w;
+      MOE_TRY(mark(2));
+      HIP_TRY(launch_gemm_w4(EPI_SCATTER, MOE_DT_F32, q, g2, gm2, s));
+    } else {
+      q.C = out;
+      MOE_TRY(mark(2));
+      HIP_TRY(launch_gemm_w4(EPI_STORE, MOE_DT_BF16, q, g2, gm2, s));
+    }
+    return mark(3);
+  }
   const int dt = act_dt(c);
   const GemmShape g1 = shape1(c, T, rows, groups, I);
   const GemmShape g2 = shape2(c, rows, groups, I);
@@ -518,7 +581,7 @@ int moe_grouped_swiglu(const moe_config* c, int64_t T, const void* hidden, const
   MOE_TRY(check_T(c, T));
   if (epilogue != MOE_EPI_STORE_ROWS && epilogue != MOE_EPI_SCATTER_ADD) return MOE_ERR_INVALID_ARG;
   if (!hidden || !expert_offsets || !w13 || !w2) return MOE_ERR_INVALID_ARG;
-  if (is_fp8(c) && (!w13_scales || !w2_scales)) return MOE_ERR_INVALID_ARG;
+  if (has_scales(c) && (!w13_scales || !w2_scales)) return MOE_ERR_INVALID_ARG;
   if (hidden_scales && !is_fp8(c)) return MOE_ERR_INVALID_ARG;
   if (epilogue == MOE_EPI_STORE_ROWS && !expert_out) return MOE_ERR_INVALID_ARG;
   if (epilogue == MOE_EPI_SCATTER_ADD && (!acc || !topk_w || !inv_perm)) return MOE_ERR_INVALID_ARG;
@@ -556,9 +619,9 @@ int moe_forward(const moe_config* c, int64_t T, const void* hidden, const void* 
   MOE_TRY(check_cfg(c));
   MOE_TRY(check_T(c, T));
   if (!hidden || !gate_w || !w13 || !w2 || !out) return MOE_ERR_INVALID_ARG;
-  if (is_fp8(c) && (!w13_scales || !w2_scales)) return MOE_ERR_INVALID_ARG;
+  if (has_scales(c) && (!w13_scales || !w2_scales)) return MOE_ERR_INVALID_ARG;
   if (c->shared_inter > 0 && (!sh_w13 || !sh_w2)) return MOE_ERR_INVALID_ARG;
-  if (c->shared_inter > 0 && is_fp8(c) && (!sh_w13_scales || !sh_w2_scales)) return MOE_ERR_INVALID_ARG;
+  if (c->shared_inter > 0 && has_scales(c) && (!sh_w13_scales || !sh_w2_scales)) return MOE_ERR_INVALID_ARG;
   if (!al16(hidden, gate_w, w13, w2, sh_w13, sh_w2, out)) return MOE_ERR_INVALID_ARG;
   const int epi = opts ? opts->epilogue : MOE_EPI_STORE_ROWS;
   if (epi != MOE_EPI_STORE_ROWS && epi != MOE_EPI_SCATTER_ADD) return MOE_ERR_INVALID_ARG;

@@ -79,6 +79,34 @@ struct GemmFp8Params {
 GemmShape gemm_fp8_shape(int rows_hint, int64_t a_bytes, int64_t b_bytes);
 hipError_t launch_gemm_fp8(int epi, const GemmFp8Params& p, const GemmShape& g, int grid_m, hipStream_t s);
 
+// Grouped GEMM with 4-bit weights (two's-complement codes, two per byte, the
+// even column in the low nibble) and one fp32 scale per weight row and 128
+// columns; bf16 activations.
+struct GemmW4Params {
+  const void* A;          // bf16 activations, row src(p) at A + src(p) * K elements
+  const int32_t* a_rows;
+  const uint8_t* B;       // group g: packed codes at B + g * b_gstride bytes, [Nrows, K/2]
+  const float* b_scales;  // group g: b_scales + g * bs_gstride, [Nrows, K/128]
+  int64_t b_gstride;
+  int64_t bs_gstride;
+  const uint8_t* B2;      // if not NULL: codes and scales of group b2_group
+  const float* b2_scales;
+  int b2_group;
+  int K;
+  int N;
+  void* C;
+  const int32_t* c_rows;
+  const float* row_w;
+  const int4* tiles;
+  const int* n_mtiles_dev;
+  int n_mtiles;
+  int M;
+  int ntn;
+  int64_t a_nrows;
+};
+GemmShape gemm_w4_shape();
+hipError_t launch_gemm_w4(int epi, int odt, const GemmW4Params& p, const GemmShape& g, int grid_m, hipStream_t s);
+
 struct RouteParams {
   const float* logits;    // [T,E] router logits, or scores when scores_given;
                           // n_parts > 1: partial logits of K slices, part_stride apart

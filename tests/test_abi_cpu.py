@@ -46,6 +46,7 @@ def cfg(**kw):
 @pytest.mark.parametrize("kw,status", [
     ({}, 0),
     (dict(dtype="fp8"), 0),
+    (dict(dtype="w4a16"), 0),
     (dict(dtype="f32"), 0),
     (dict(n_group=7), -2),                    # E % n_group
     (dict(topk_group=9), -2),                 # topk_group > n_group
@@ -56,6 +57,8 @@ def cfg(**kw):
     (dict(routed_scaling_factor=float("inf")), -2),
     (dict(hidden=7168 + 32), -3),             # not a multiple of 64
     (dict(dtype="fp8", inter=2048 + 64), -3), # FP8 needs multiples of 128
+    (dict(dtype="w4a16", hidden=7168 + 64), -3),  # so do 4-bit weights (128-column groups)
+    (dict(dtype="w4a16", shared_inter=2048 + 64), -3),
     (dict(n_experts=2048, n_group=8), -3),    # E > 1024
     (dict(top_k=33, topk_group=8), -3),       # k > 32
 ])
@@ -73,6 +76,12 @@ def test_bad_enums_are_invalid_args():
     c = cfg()
     c.out_dtype = 0                             # output dtype must equal the activation dtype
     assert moe.validate_config(c) == -3
+    c = cfg(dtype="f32")
+    c.weight_dtype = moe.MOE_INT4               # 4-bit weights take bf16 activations only
+    assert moe.validate_config(c) == -3
+    c = cfg()
+    c.weight_dtype = 4
+    assert moe.validate_config(c) == -1
 
 
 def test_workspace_sizes():
@@ -87,6 +96,10 @@ def test_workspace_sizes():
     assert moe.workspace_size(c, T, moe.MOE_OP_ROUTE) >= T * 256 * 4
     bad = cfg(n_group=7)
     assert moe.workspace_size(bad, 128) == 0
+    # the GEMMs address hidden and intermediate rows with 32-bit byte offsets
+    assert moe.workspace_size(c, 16384) > 0
+    assert moe.workspace_size(c, 65536) == 0         # (T*k + T) * I * 2 bytes >= 2^31
+    assert moe.workspace_size(cfg(top_k=1, n_group=1, topk_group=1, shared_inter=0), 160000) == 0  # T*H*2 >= 2^31
 
 
 def _call(fn, *args):
@@ -119,6 +132,15 @@ def test_entry_points_reject_before_launch():
     fp8 = cfg(dtype="fp8")
     assert L.moe_grouped_swiglu(b(fp8), 16, p, null, p, p, p, null, p, null, 0, null, null, p, null, p,
                                 1 << 30, null) == -1      # FP8 without scales
+    w4 = cfg(dtype="w4a16")
+    assert L.moe_grouped_swiglu(b(w4), 16, p, null, p, p, p, null, p, p, 0, null, null, p, null, p,
+                                1 << 30, null) == -1      # 4-bit weights without w13 scales
+    assert L.moe_grouped_swiglu(b(w4), 16, p, p, p, p, p, p, p, p, 0, null, null, p, null, p,
+                                1 << 30, null) == -1      # activation scales with bf16 activations
+    assert L.moe_forward(b(w4), 16, p, p, null, p, p, p, p, p, null, p, p, p, null, p, 1 << 40,
+                         null) == -1      # shared 4-bit weights without scales
+    assert L.moe_forward(b(c), 1 << 20, p, p, null, p, null, p, null, p, null, p, null, p, null, p, 1 << 40,
+                         null) == -3      # activations past 2^31 bytes
     assert L.moe_combine(b(c), 16, p, null, null, p, null, p, null) == -1   # rows without inv_perm
     assert L.moe_combine(b(c), 16, null, null, null, null, null, null, null) == -1
     assert L.moe_forward(b(c), 16, p, p, null, p, null, p, null, null, null, null, null, p, null, p, 1 << 40,

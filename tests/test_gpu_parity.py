@@ -222,6 +222,14 @@ SMALL = {
                                     shared_inter=256),
     "fp8_small": _reduced("v3_fp8", tokens=300, hidden=1024, inter=256, n_experts=64, shared_inter=256),
     "fp8_small_ragged": _reduced("v3_fp8", tokens=45, hidden=512, inter=384, n_experts=64, shared_inter=128),
+    # 4-bit weights: shared expert merged as one more group (Is == I, T <= 1024)
+    "w4_small": _reduced("v3_decode_w4a16", tokens=300, hidden=1024, inter=256, n_experts=64, shared_inter=256,
+                         bias="zero"),
+    # 4-bit weights: H a ragged number of 256-row n-tiles, a separate shared expert (Is != I)
+    "w4_ragged": _reduced("v3_decode_w4a16", tokens=45, hidden=640, inter=384, n_experts=16, n_group=4,
+                          topk_group=2, top_k=4, shared_inter=128, bias="zero"),
+    # 4-bit weights, decode batch with the Zipf-skewed load: many empty and one-row experts
+    "w4_decode_like": _reduced("v3_decode_w4a16", hidden=1024, inter=256, shared_inter=256),
 }
 
 
@@ -350,7 +358,7 @@ def test_staged_calls_match_forward():
 # ------------------------------------------------------ full-size workloads ---
 
 @pytest.mark.parametrize("name,samples", [("v2_lite_bf16", 8), ("v3_prefill_bf16", 6), ("v3_decode_bf16", 8),
-                                          ("v3_fp8", 4)])
+                                          ("v3_fp8", 4), ("v3_decode_w4a16", 8)])
 def test_forward_full_size_sampled(name, samples):
     """The workload at its full size, in the launch configuration the
     benchmark times: routing and permutation bit-exact on every token, layer
@@ -438,7 +446,7 @@ def test_load_balance_matches_oracle(mode, T, E, k):
     assert st.cv == pytest.approx(ref["cv"], rel=1e-6, abs=1e-12)
 
 
-@pytest.mark.parametrize("name", ["v3_small", "fp8_small", "v2_lite_small"])
+@pytest.mark.parametrize("name", ["v3_small", "fp8_small", "v2_lite_small", "w4_small"])
 def test_forward_is_deterministic(name):
     """With the row-store epilogue the layer output is bitwise reproducible:
     fixed split-K slice order in the router, fixed K order in every GEMM and a
@@ -458,7 +466,7 @@ def test_forward_is_deterministic(name):
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
-@pytest.mark.parametrize("name", ["v3_small", "fp8_small"])
+@pytest.mark.parametrize("name", ["v3_small", "fp8_small", "w4_small"])
 def test_forward_in_a_hip_graph(name):
     """moe_forward allocates nothing and never synchronises, so a whole layer can
     be captured into a HIP graph: every replay, with eager work in between,
