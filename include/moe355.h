@@ -67,7 +67,8 @@ typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_scoring;
  * W4A16), two's complement in [-8, 7], two per byte: input column 2j in the
  * low nibble (bits 0-3) of byte j of its row, column 2j+1 in the high nibble;
  * a weight matrix stored (out, in) is (out, in/2) bytes, with one fp32 scale
- * per output row and 128 input columns, (out, in/128); value = q * scale. */
+ * per output row and 128 input columns, stored group-major, (in/128, out);
+ * value = q * scale. */
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_INT4 = 3 } moe_dtype;
 
 typedef enum { MOE_EPI_STORE_ROWS = 0, MOE_EPI_SCATTER_ADD = 1 } moe_epilogue;
@@ -212,7 +213,7 @@ int moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_ids,
  *   w13, w2        weight_dtype; w13_scales [E,2I/128,H/128] and
  *                  w2_scales [E,H/128,I/128] fp32 for FP8 weights;
  *                  4-bit weights: w13 [E,2I,H/2] and w2 [E,H,I/2] bytes with
- *                  w13_scales [E,2I,H/128] and w2_scales [E,H,I/128] fp32;
+ *                  w13_scales [E,H/128,2I] and w2_scales [E,I/128,H] fp32;
  *                  NULL for bf16 / fp32 weights
  *   epilogue       MOE_EPI_STORE_ROWS: expert_out[p] = y_p, [T*k,H] act_dtype
  *                  MOE_EPI_SCATTER_ADD: acc[permuted_src[p]] += w_p * y_p with
@@ -251,7 +252,7 @@ int moe_combine(const moe_config* cfg, int64_t T, const void* expert_out, const 
  *   hidden [T,H], gate_w [E,H] act_dtype; bias [E] fp32 or NULL;
  *   w13, w2 (+ scales) as in moe_grouped_swiglu; sh_w13 [2Is,H], sh_w2 [H,Is]
  *   (+ scales [2Is/128,H/128], [H/128,Is/128] for FP8; packed [2Is,H/2],
- *   [H,Is/2] with scales [2Is,H/128], [H,Is/128] for 4-bit weights), NULL
+ *   [H,Is/2] with scales [H/128,2Is], [Is/128,H] for 4-bit weights), NULL
  *   when Is == 0;
  *   out [T,H] act_dtype; opts may be NULL (store-rows epilogue, no extra
  *   outputs).

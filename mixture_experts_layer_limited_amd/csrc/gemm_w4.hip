@@ -3,30 +3,39 @@
 // zhiyuanblog.org/blog/moe-inference, §8 quantisation table), for the
 // grouped-GEMM step of the same walkthrough (§3.3):
 //
-//   C[p, n] = sum_kb s[n, kb] * sum_{k in group kb} A[src(p), k] * q[n, k]
+//   C[p, n] = sum_g s[g, n] * sum_{k in group g} A[src(p), k] * q[n, k]
 //
 // with q the signed 4-bit codes (two per byte, the even column in the low
-// nibble) and s one fp32 scale per weight row and 128 columns.
+// nibble) and s one fp32 scale per weight row and 128 columns, stored
+// group-major.
 //
 // Design (decode-sized groups, where the weight stream is the whole cost):
-//   * one K step is one scale group (128 columns): the activation rows (32 x
-//     256 bytes), the packed codes (BN x 64 bytes) and the BN scales of the
-//     step stream straight from memory into one LDS ring slot with
-//     buffer_load ... lds, S - 1 steps ahead of the MFMAs;
+//   * tiles of 16 rows (decode experts hold a few rows each);
+//   * one K step is two scale groups (256 columns); the packed codes (BN rows
+//     x 128 bytes: one whole cache line per weight row) with the 2 x BN
+//     scales of the step (two contiguous runs), and the activation rows (16 x
+//     512 bytes), stream straight from memory into LDS rings with
+//     buffer_load ... lds: the weight ring SB - 1 steps ahead of the MFMAs,
+//     the activation ring (mostly L2 hits) SA - 1 steps ahead, so the LDS goes
+//     to weight bytes in flight;
 //   * codes widen to bf16 with two bit operations per pair: a nibble n, its
 //     sign bit flipped (u = n ^ 8 = q + 8), or-ed under the bf16 pattern of
 //     128 reads as 128 + u = 136 + q exactly; a pair of nibbles four apart in
 //     one dword widens in one and + xor, so the B fragment holds the columns
 //     of its 8-column run in the order 0,4,1,5,2,6,3,7 and the activation
-//     fragment is reordered to match (a dot product does not see the order);
+//     fragment is permuted to match (a dot product does not see the order);
 //   * the offset is removed exactly inside the MFMA chain: each group's
 //     accumulation starts from A * (-136) (the same activation fragments
 //     against a constant bf16 -136), so the chain ends at sum A*q in fp32;
 //     the group's scale then folds into the fp32 accumulator (one FMA per
 //     element and group);
-//   * 4 waves share the tile's 32 activation rows; wave w owns TN 32-column
-//     blocks of weight rows (SwiGLU: TN/2 gate blocks and the matching up
-//     blocks), so the SiLU * up epilogue needs no data exchange.
+//   * the MFMAs are 16 x 16 x 32 (one row block per tile);
+//   * 8 waves share the tile's 16 activation rows: wave w owns 2 TN 16-column
+//     blocks of weight rows (SwiGLU: TN gate blocks and the matching up
+//     blocks, so the SiLU * up epilogue needs no data exchange between
+//     column blocks) for group w / 4 of every step; the two waves of a
+//     column block share a SIMD, where one's MFMAs overlap the other's code
+//     widening, and their sums meet once, through LDS, before the epilogue.
 #include "common.h"
 #include "kernels.h"
 #include "lds_dma.h"
@@ -49,38 +58,49 @@ __device__ __forceinline__ u32x4 widen_w4(uint32_t w) {
 }
 
 // Eight consecutive bf16 activations (pairs (0,1), (2,3), (4,5), (6,7)) in
-// the order of widen_w4: pairs (0,4), (1,5), (2,6), (3,7).
+// the order of widen_w4: pairs (0,4), (1,5), (2,6), (3,7).  v_perm_b32 picks
+// bytes 0-3 from its second operand and 4-7 from its first.
 __device__ __forceinline__ u32x4 reorder_a(u32x4 a) {
   u32x4 r;
-  r[0] = (a[0] & 0xFFFFu) | (a[2] << 16);
-  r[1] = (a[0] >> 16) | (a[2] & 0xFFFF0000u);
-  r[2] = (a[1] & 0xFFFFu) | (a[3] << 16);
-  r[3] = (a[1] >> 16) | (a[3] & 0xFFFF0000u);
+  r[0] = __builtin_amdgcn_perm(a[2], a[0], 0x05040100u);
+  r[1] = __builtin_amdgcn_perm(a[2], a[0], 0x07060302u);
+  r[2] = __builtin_amdgcn_perm(a[3], a[1], 0x05040100u);
+  r[3] = __builtin_amdgcn_perm(a[3], a[1], 0x07060302u);
   return r;
 }
 
 }  // namespace
 
-template <int TN, int S, int EPI, int ODT>
-__global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmW4Params p) {
-  constexpr int NW = 4, BM = 32, BN = NW * TN * 32;
-  constexpr int KS = 128;                        // K per step = one scale group
-  constexpr int AROW = KS * 2, BROW = KS / 2;    // bytes per row per step: bf16 / packed 4-bit
-  constexpr int ABYTES = BM * AROW, BBYTES = BN * BROW, SBYTES = BN * 4;
-  constexpr int SLOT = ABYTES + BBYTES + SBYTES;
-  constexpr int AI = ABYTES / 1024 / NW;         // 16-byte-per-lane DMAs per wave per slot
+// Two waves per SIMD (256 registers each): the MFMAs write VGPRs and the
+// scale fold reads them without copies.  LDS holds one work-group per CU.
+template <int TN, int SA, int SB, int EPI, int ODT>
+__global__ __launch_bounds__(512, 1) void gemm_w4_kernel(GemmW4Params p) {
+  constexpr int NW = 8, WN = 4, BM = 16, BN = WN * TN * 32;
+  constexpr int G = NW / WN;                      // scale groups per K step, one per wave set
+  constexpr int KS = 128 * G;                     // K per step
+  constexpr int AROW = KS * 2, BROW = KS / 2;     // bytes per row per step: bf16 / packed 4-bit
+  constexpr int ACH = AROW / 16, BCH = BROW / 16; // 16-byte chunks per row
+  constexpr int ABYTES = BM * AROW, BBYTES = BN * BROW, SBYTES = G * BN * 4;
+  constexpr int ASLOT = ABYTES, BSLOT = BBYTES + SBYTES;  // activation slot; codes + scales slot
+  constexpr int BRING = SA * ASLOT;                       // the weight ring follows the activation ring
+  constexpr int AI = ABYTES / 1024 / NW;          // 16-byte-per-lane DMAs per wave per slot
   constexpr int BI = BBYTES / 1024 / NW;
-  constexpr int SI = SBYTES / 256 / NW;          // 4-byte-per-lane DMAs (scales)
+  constexpr int SI = SBYTES / 256 / NW;           // 4-byte-per-lane DMAs (scales)
   constexpr int LI = AI + BI + SI;
+  // At the top of step kt the last DMAs issued are A(kt) then B(kt + SB - SA);
+  // B(kt) went out SB - SA steps before A(kt), so waiting for A(kt) covers it.
+  constexpr int VMN = (BI + SI) + (SA - 2) * LI;
   static_assert(AI * 1024 * NW == ABYTES && BI * 1024 * NW == BBYTES && SI * 256 * NW == SBYTES, "tile / wave");
+  static_assert(ACH == 32 && BCH == 8 && BN % 64 == 0, "row layout");
   static_assert(EPI != EPI_SWIGLU || TN % 2 == 0, "SwiGLU pairs gate and up blocks");
-  static_assert(S >= 2 && (S - 2) * LI < 64, "ring depth");
+  static_assert(SA >= 2 && SB >= SA && VMN < 64, "ring depths");
 
   extern __shared__ __attribute__((aligned(16))) char lds[];
   lds_char* const lds3 = (lds_char*)lds;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave % WN, kset = wave / WN;  // column blocks and scale group of this wave
 
   const int total = p.tiles ? *p.n_mtiles_dev : p.n_mtiles * p.ntn;
   const int P = blockIdx.x;
@@ -98,14 +118,15 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmW4Params p) {
   const int rows = r1 - r0;
   const int64_t arow = (int64_t)p.K * 2;  // bytes per activation row
   const int64_t brow = p.K / 2;           // bytes per packed weight row
-  const int nk = p.K / KS;                // steps = scale groups per row
+  const int ngroups = p.K / 128;          // scale groups per row
+  const int nk = (ngroups + G - 1) / G;   // steps; an odd group count leaves the last step half full
   const bool second = p.B2 && grp == p.b2_group;
   const uint8_t* Bg = second ? p.B2 : p.B + (int64_t)grp * p.b_gstride;
   const float* Sg = second ? p.b2_scales : p.b_scales + (int64_t)grp * p.bs_gstride;
   const int b_nrows = (EPI == EPI_SWIGLU) ? 2 * p.N : p.N;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, p.a_nrows * arow);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bg, (int64_t)b_nrows * brow);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(Sg, (int64_t)b_nrows * nk * 4);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(Sg, (int64_t)ngroups * b_nrows * 4);
 
   // Weight row of tile row r (clamped: rows past N are computed and dropped).
   auto wrow_of = [&](int r) {
@@ -117,14 +138,15 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmW4Params p) {
     }
   };
 
-  // Per-lane source offsets, fixed over K.  A: 4 rows of 16 chunks per DMA,
-  // chunk c of row r stored at chunk c ^ (r & 15); B: 16 rows of 4 chunks,
-  // chunk c at c ^ swz<64>(r); scales: 64 rows per DMA, 4 bytes each.
+  // Per-lane source offsets, fixed over K.  A: 2 rows of 32 chunks per DMA,
+  // chunk c of row r stored at chunk c ^ (r & 15); B: 8 rows of 8 chunks,
+  // chunk c at c ^ swz<128>(r); scales: 64 consecutive entries of one group
+  // per DMA, 4 bytes each (the slot holds group 0's BN scales, then group 1's).
   uint32_t voa[AI], vob[BI], vos[SI];
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
-    const int r = (wave * AI + i) * 4 + (lane >> 4);
-    const int chunk = (lane & 15) ^ (r & 15);
+    const int r = (wave * AI + i) * (64 / ACH) + lane / ACH;
+    const int chunk = (lane % ACH) ^ (r & 15);
     if (r < rows) {
       const int src = p.a_rows ? p.a_rows[r0 + r] : r0 + r;
       voa[i] = (uint32_t)((int64_t)src * arow + chunk * 16);
@@ -134,143 +156,180 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmW4Params p) {
   }
 #pragma unroll
   for (int i = 0; i < BI; ++i) {
-    const int r = (wave * BI + i) * 16 + (lane >> 2);
-    const int chunk = (lane & 3) ^ swz<64>(r);
+    const int r = (wave * BI + i) * (64 / BCH) + lane / BCH;
+    const int chunk = (lane % BCH) ^ swz<128>(r);
     vob[i] = (uint32_t)((int64_t)wrow_of(r) * brow + chunk * 16);
   }
 #pragma unroll
-  for (int i = 0; i < SI; ++i) vos[i] = (uint32_t)((int64_t)wrow_of((wave * SI + i) * 64 + lane) * nk * 4);
+  for (int i = 0; i < SI; ++i) {
+    const int idx = (wave * SI + i) * 64 + lane;
+    vos[i] = (uint32_t)(((int64_t)(idx / BN) * b_nrows + wrow_of(idx % BN)) * 4);
+  }
 
-  // Step kt into slot kt % S; past the last step every offset is out of range
+  // Step kt of each ring; past the last step every offset is out of range
   // (zero fill, no traffic), so the instruction count per step stays fixed.
-#define MOE_W4_ISSUE(kt_)                                                                          \
+  // In a half-full last step the second group's bytes are not used.
+#define MOE_W4_ISSUE_A(kt_)                                                                        \
   do {                                                                                             \
-    lds_char* slot_ = lds3 + ((kt_) % S) * SLOT;                                                   \
-    const bool live_ = (kt_) < nk;                                                                 \
-    const uint32_t sa_ = live_ ? (uint32_t)(kt_) * AROW : 0x80000000u;                             \
-    const uint32_t sb_ = live_ ? (uint32_t)(kt_) * BROW : 0x80000000u;                             \
-    const uint32_t ss_ = live_ ? (uint32_t)(kt_) * 4 : 0x80000000u;                                \
+    lds_char* slot_ = lds3 + ((kt_) % SA) * ASLOT;                                                 \
+    const uint32_t sa_ = (kt_) < nk ? (uint32_t)(kt_) * AROW : 0x80000000u;                        \
     _Pragma("unroll") for (int i = 0; i < AI; ++i) dma16(ra, slot_ + (wave * AI + i) * 1024, voa[i], sa_); \
+  } while (0)
+#define MOE_W4_ISSUE_B(kt_)                                                                        \
+  do {                                                                                             \
+    lds_char* slot_ = lds3 + BRING + ((kt_) % SB) * BSLOT;                                         \
+    const bool live_ = (kt_) < nk;                                                                 \
+    const uint32_t sb_ = live_ ? (uint32_t)(kt_) * BROW : 0x80000000u;                             \
+    const uint32_t ss_ = live_ ? (uint32_t)(kt_) * G * b_nrows * 4 : 0x80000000u;                  \
     _Pragma("unroll") for (int i = 0; i < BI; ++i)                                                 \
-      dma16(rb, slot_ + ABYTES + (wave * BI + i) * 1024, vob[i], sb_);                             \
+      dma16(rb, slot_ + (wave * BI + i) * 1024, vob[i], sb_);                                      \
     _Pragma("unroll") for (int i = 0; i < SI; ++i)                                                 \
-      dma4(rs, slot_ + ABYTES + BBYTES + (wave * SI + i) * 256, vos[i], ss_);                      \
+      dma4(rs, slot_ + BBYTES + (wave * SI + i) * 256, vos[i], ss_);                               \
   } while (0)
 
-  auto bblock = [&](int j) {
+  // 16-column blocks: NB per wave (SwiGLU: NB/2 gate blocks, then the
+  // matching up blocks); first B-tile row of block j of this wave.
+  constexpr int NB = 2 * TN;
+  auto bbase = [&](int j) {
     if constexpr (EPI == EPI_SWIGLU)
-      return j < TN / 2 ? wave * (TN / 2) + j : NW * (TN / 2) + wave * (TN / 2) + (j - TN / 2);
+      return j < NB / 2 ? (wn * (NB / 2) + j) * 16 : BN / 2 + (wn * (NB / 2) + (j - NB / 2)) * 16;
     else
-      return wave * TN + j;
+      return (wn * NB + j) * 16;
   };
 
-  const int lr = lane & 31, hi = lane >> 5;
+  // 16 x 16 x 32 MFMA lanes: l = 16 q + n takes activation row n and weight
+  // row n of a block, columns 8 q .. 8 q + 7 of each 32-column sub-step.
+  const int n16 = lane & 15, q = lane >> 4;
   const u32x4 kneg = {0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u};  // bf16 -136 everywhere
 
-  f32x16 acc[TN];
+  f32x4 acc[NB];
 #pragma unroll
-  for (int j = 0; j < TN; ++j)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[j][e] = 0.0f;
+  for (int j = 0; j < NB; ++j) acc[j] = {0.0f, 0.0f, 0.0f, 0.0f};
 
+  // The issues of the SB - 1 steps before step 0, in steady-state order.
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s) MOE_W4_ISSUE(s);
+  for (int t = -(SB - 1); t < 0; ++t) {
+    if (t + SA - 1 >= 0) MOE_W4_ISSUE_A(t + SA - 1);
+    MOE_W4_ISSUE_B(t + SB - 1);
+  }
 
   for (int kt = 0; kt < nk; ++kt) {
-    wait_vm_barrier<(S - 2) * LI>();  // slot kt landed; every wave is done with slot kt - 1
-    const char* slot = lds + (kt % S) * SLOT;
-    // Lane (row lr, half hi) takes columns [64 hi, 64 hi + 64) of the group:
-    // activation chunk 8 hi + st and code dword st for sub-step st.
-    u32x4 a[8];
+    wait_vm_barrier<VMN>();  // step kt landed; every wave is done with step kt - 1
+    const char* aslot = lds + (kt % SA) * ASLOT;
+    const char* bslot = lds + BRING + (kt % SB) * BSLOT;
+    const int g = kset;
+    const bool live = kt * G + g < ngroups;  // wave-uniform: false only in a half-full last step
+    // Lane (n, q) takes columns [32 q, 32 q + 32) of group g: activation
+    // chunk 16 g + 4 q + st and code dword st (of chunk 4 g + q) for sub-step st.
+    u32x4 a[4];
+    u32x4 b[NB];
+    float sc[NB];
+    if (live) {
 #pragma unroll
-    for (int st = 0; st < 8; ++st)
-      a[st] = *(const u32x4*)(slot + lr * AROW + (((8 * hi + st) ^ (lr & 15)) * 16));
-    u32x4 b[TN][2];
-    float sc[TN];
+      for (int st = 0; st < 4; ++st)
+        a[st] = *(const u32x4*)(aslot + n16 * AROW + (((16 * g + 4 * q + st) ^ n16) * 16));
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int row = bblock(j) * 32 + lr;
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        b[j][c] = *(const u32x4*)(slot + ABYTES + row * BROW + (((2 * hi + c) ^ swz<64>(row)) * 16));
-      sc[j] = *(const float*)(slot + ABYTES + BBYTES + row * 4);
+      for (int j = 0; j < NB; ++j) {
+        const int row = bbase(j) + n16;
+        b[j] = *(const u32x4*)(bslot + row * BROW + (((4 * g + q) ^ swz<128>(row)) * 16));
+        sc[j] = *(const float*)(bslot + BBYTES + (g * BN + row) * 4);
+      }
     }
-    MOE_W4_ISSUE(kt + S - 1);  // after the reads in program order: refills slot kt - 1
-
-    f32x16 base;
+    // after the reads in program order: refill the slots of step kt - 1
+    MOE_W4_ISSUE_A(kt + SA - 1);
+    MOE_W4_ISSUE_B(kt + SB - 1);
+    if (live) {
+      f32x4 base = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int e = 0; e < 16; ++e) base[e] = 0.0f;
+      for (int st = 0; st < 4; ++st)
+        base = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[st]),
+                                                       __builtin_bit_cast(bf16x8, kneg), base, 0, 0, 0);
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      a[st] = reorder_a(a[st]);
-      base = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[st]),
-                                                     __builtin_bit_cast(bf16x8, kneg), base, 0, 0, 0);
-    }
+      for (int st = 0; st < 4; ++st) a[st] = reorder_a(a[st]);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      f32x16 part = base;
+      for (int j = 0; j < NB; ++j) {
+        f32x4 part = base;
 #pragma unroll
-      for (int st = 0; st < 8; ++st)
-        part = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[st]),
-                                                       __builtin_bit_cast(bf16x8, widen_w4(b[j][st >> 2][st & 3])),
-                                                       part, 0, 0, 0);
+        for (int st = 0; st < 4; ++st)
+          part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[st]),
+                                                         __builtin_bit_cast(bf16x8, widen_w4(b[j][st])), part, 0, 0, 0);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[j][e] = fmaf(sc[j], part[e], acc[j][e]);
+        for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(sc[j], part[r], acc[j][r]);
+      }
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the tail's zero-fill DMAs
-#undef MOE_W4_ISSUE
+#undef MOE_W4_ISSUE_A
+#undef MOE_W4_ISSUE_B
 
-  // Epilogue.  Lane l, register e of a 32x32 block: row 8*(e/4) + 4*(l/32) + e%4, column l%32.
+  // The second wave set hands its sums to the first through the (now idle)
+  // ring: block j of lane l of column group wn at (j * WN + wn) * 64 + l.
+  __syncthreads();
+  f32x4* red = (f32x4*)lds;
+  if (kset == 1) {
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int row = 8 * (e >> 2) + 4 * hi + (e & 3);
+    for (int j = 0; j < NB; ++j) red[(j * WN + wn) * 64 + lane] = acc[j];
+  }
+  __syncthreads();
+  if (kset == 1) return;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const f32x4 v = red[(j * WN + wn) * 64 + lane];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[j][r] += v[r];
+  }
+
+  // Epilogue.  Lane l = 16 q + n, register r of a 16 x 16 block: row 4 q + r, column n.
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 4 * q + r;
     if (row >= rows) continue;
     const int prow = r0 + row;
     if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
-      for (int j = 0; j < TN / 2; ++j) {
-        const int col = nt * (BN / 2) + (wave * (TN / 2) + j) * 32 + lr;
+      for (int j = 0; j < NB / 2; ++j) {
+        const int col = nt * (BN / 2) + (wn * (NB / 2) + j) * 16 + n16;
         if (col < p.N)
           Elem<ODT>::store((typename Elem<ODT>::T*)p.C, (int64_t)prow * p.N + col,
-                           silu_mul_w4(acc[j][e], acc[j + TN / 2][e]));
+                           silu_mul_w4(acc[j][r], acc[j + NB / 2][r]));
       }
     } else if constexpr (EPI == EPI_SCATTER) {
       const int tok = p.c_rows ? p.c_rows[prow] : prow;
       const float w = p.row_w[prow];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int col = nt * BN + bblock(j) * 32 + lr;
-        if (col < p.N) atomicAdd((float*)p.C + (int64_t)tok * p.N + col, w * acc[j][e]);
+      for (int j = 0; j < NB; ++j) {
+        const int col = nt * BN + bbase(j) + n16;
+        if (col < p.N) atomicAdd((float*)p.C + (int64_t)tok * p.N + col, w * acc[j][r]);
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int col = nt * BN + bblock(j) * 32 + lr;
-        if (col < p.N) Elem<ODT>::store((typename Elem<ODT>::T*)p.C, (int64_t)prow * p.N + col, acc[j][e]);
+      for (int j = 0; j < NB; ++j) {
+        const int col = nt * BN + bbase(j) + n16;
+        if (col < p.N) Elem<ODT>::store((typename Elem<ODT>::T*)p.C, (int64_t)prow * p.N + col, acc[j][r]);
       }
     }
   }
 }
 
-template <int TN, int S, int EPI, int ODT>
+template <int TN, int SA, int SB, int EPI, int ODT>
 static hipError_t launch_w4(const GemmW4Params& p, int grid_m, hipStream_t s) {
   constexpr int BN = 4 * TN * 32;
-  constexpr int lds_bytes = S * (32 * 256 + BN * 64 + BN * 4);
+  constexpr int lds_bytes = SA * 16 * 512 + SB * (BN * 128 + 2 * BN * 4);
   static_assert(lds_bytes <= 160 * 1024, "LDS");
+  static_assert(2 * TN * 4 * 64 * 16 <= lds_bytes, "reduction space");
   {
-    const hipError_t e = allow_lds<gemm_w4_kernel<TN, S, EPI, ODT>>(lds_bytes);
+    const hipError_t e = allow_lds<gemm_w4_kernel<TN, SA, SB, EPI, ODT>>(lds_bytes);
     if (e != hipSuccess) return e;
   }
   const int64_t grid = (int64_t)grid_m * p.ntn;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_w4_kernel<TN, S, EPI, ODT>), dim3((unsigned)grid), dim3(256), lds_bytes, s, p);
+  hipLaunchKernelGGL((gemm_w4_kernel<TN, SA, SB, EPI, ODT>), dim3((unsigned)grid), dim3(512), lds_bytes, s, p);
   return hipGetLastError();
 }
 
 GemmShape gemm_w4_shape() {
   GemmShape g;
-  g.bm = 32;
+  g.bm = 16;
   g.bn = 256;
   g.kind = 0;
   return g;
@@ -279,11 +338,11 @@ GemmShape gemm_w4_shape() {
 hipError_t launch_gemm_w4(int epi, int odt, const GemmW4Params& p, const GemmShape& g, int grid_m, hipStream_t s) {
   if (g.kind != 0) return hipErrorInvalidValue;
   switch (epi) {
-    case EPI_SWIGLU: return launch_w4<2, 6, EPI_SWIGLU, MOE_DT_BF16>(p, grid_m, s);
-    case EPI_SCATTER: return launch_w4<2, 6, EPI_SCATTER, MOE_DT_F32>(p, grid_m, s);
+    case EPI_SWIGLU: return launch_w4<2, 2, 4, EPI_SWIGLU, MOE_DT_BF16>(p, grid_m, s);
+    case EPI_SCATTER: return launch_w4<2, 2, 4, EPI_SCATTER, MOE_DT_F32>(p, grid_m, s);
     default:
-      if (odt == MOE_DT_F32) return launch_w4<2, 6, EPI_STORE, MOE_DT_F32>(p, grid_m, s);
-      return launch_w4<2, 6, EPI_STORE, MOE_DT_BF16>(p, grid_m, s);
+      if (odt == MOE_DT_F32) return launch_w4<2, 2, 4, EPI_STORE, MOE_DT_F32>(p, grid_m, s);
+      return launch_w4<2, 2, 4, EPI_STORE, MOE_DT_BF16>(p, grid_m, s);
   }
 }
 

@@ -25,8 +25,9 @@ Distributions:
     not part of the layer.
   * W4A16 workloads store expert weights as signed 4-bit integers, two per
     byte (even input column in the low nibble), with one fp32 scale per
-    output row and 128 input columns (walkthrough §8 quantisation table
-    names the format; the packing and grouping are this library's reading).
+    output row and 128 input columns, stored group-major (in/128, out)
+    (walkthrough §8 quantisation table names the format; the packing and
+    grouping are this library's reading).
     The conversion is done here, offline: symmetric, scale = amax / 7 (1 for
     an all-zero group), q = round-half-even(w / scale), clamped to [-8, 7].
 
@@ -183,7 +184,7 @@ def fp8_block_quantize(w: torch.Tensor):
 
 
 def int4_group_quantize(w: torch.Tensor):
-    """Packed signed 4-bit codes (n, k/2) uint8 and fp32 scales (n, k/128) of a
+    """Packed signed 4-bit codes (n, k/2) uint8 and fp32 scales (k/128, n) of a
     2-D fp32 weight: one symmetric scale per row and 128 columns."""
     n, k = w.shape
     if k % 128:
@@ -194,7 +195,7 @@ def int4_group_quantize(w: torch.Tensor):
     q = torch.round(g / scale[:, :, None]).clamp_(-8, 7).to(torch.int16).reshape(n, k)
     nib = q & 0xF
     packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).to(torch.uint8)
-    return packed.contiguous(), scale.contiguous()
+    return packed.contiguous(), scale.t().contiguous()
 
 
 def _stacked(cfg: LayerConfig, name: str, n_out: int, n_in: int, count: int, seed: int,
@@ -203,7 +204,7 @@ def _stacked(cfg: LayerConfig, name: str, n_out: int, n_in: int, count: int, see
     std = n_in ** -0.5
     if cfg.dtype == "w4a16":
         codes = torch.empty(count, n_out, n_in // 2, dtype=torch.uint8, device=device)
-        scales = torch.empty(count, n_out, n_in // 128, dtype=torch.float32, device=device)
+        scales = torch.empty(count, n_in // 128, n_out, dtype=torch.float32, device=device)
         for e in range(count):
             c, s = int4_group_quantize(_normal((n_out, n_in), std, seed, name, e, device))
             codes[e].copy_(c)
@@ -229,7 +230,7 @@ def expert_weights(cfg: LayerConfig, seed: int = 0, device="cpu") -> Dict[str, O
     up rows [I,2I) (walkthrough §2.2, §3.3.1).  FP8 configs also return block
     scales w13_s (E,2I/128,H/128), w2_s (E,H/128,I/128), sh_w13_s, sh_w2_s.
     W4A16 configs return packed codes w13 (E,2I,H/2), w2 (E,H,I/2) and group
-    scales w13_s (E,2I,H/128), w2_s (E,H,I/128) (shared: without the E axis)."""
+    scales w13_s (E,H/128,2I), w2_s (E,I/128,H) (shared: without the E axis)."""
     fp8 = cfg.dtype == "fp8"
     E, H, I, Is = cfg.n_experts, cfg.hidden, cfg.inter, cfg.shared_inter
     w13, w13_s = _stacked(cfg, "w13", 2 * I, H, E, seed, device, fp8)

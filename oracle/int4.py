@@ -11,7 +11,8 @@ Readings taken where they are silent:
     high nibble (bits 4-7): packed shape (out, in/2), uint8;
   * one fp32 scale per output row and per group of 128 consecutive input
     columns (the 128-wide granularity the FP8 recipe uses for activation
-    tiles): scales shape (out, in/128); value = q * scale, exact in fp64;
+    tiles), stored group-major as 4-bit checkpoints commonly store them:
+    scales shape (in/128, out); value = q * scale, exact in fp64;
   * activations stay in the activation dtype (bf16) and are not quantised.
 """
 from __future__ import annotations
@@ -39,12 +40,12 @@ def unpack_int4(packed: np.ndarray) -> np.ndarray:
 
 
 def dequantize_int4_groups(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """(rows, cols) fp64 weight: q[r, c] * scales[r, c // 128]."""
+    """(rows, cols) fp64 weight: q[r, c] * scales[c // 128, r]."""
     q = unpack_int4(packed)
     rows, cols = q.shape
     if cols % INT4_GROUP:
         raise ValueError("4-bit weights need a multiple of 128 input columns")
     s = np.asarray(scales, np.float64)
-    if s.shape != (rows, cols // INT4_GROUP):
-        raise ValueError(f"scales shape {s.shape}, need {(rows, cols // INT4_GROUP)}")
-    return (q.reshape(rows, cols // INT4_GROUP, INT4_GROUP) * s[:, :, None]).reshape(rows, cols)
+    if s.shape != (cols // INT4_GROUP, rows):
+        raise ValueError(f"scales shape {s.shape}, need {(cols // INT4_GROUP, rows)}")
+    return (q.reshape(rows, cols // INT4_GROUP, INT4_GROUP) * s.T[:, :, None]).reshape(rows, cols)

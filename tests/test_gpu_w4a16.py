@@ -25,7 +25,7 @@ def say(*a):
 
 def _random_w4(rng, E, n_out, n_in):
     codes = rng.integers(0, 256, size=(E, n_out, n_in // 2), dtype=np.uint8)
-    mag = rng.uniform(0.5, 1.5, size=(E, n_out, n_in // 128)) / (4.0 * np.sqrt(n_in))
+    mag = rng.uniform(0.5, 1.5, size=(E, n_in // 128, n_out)) / (4.0 * np.sqrt(n_in))
     sign = np.where(rng.uniform(size=mag.shape) < 0.25, -1.0, 1.0)
     return codes, (mag * sign).astype(np.float32)
 
@@ -87,12 +87,12 @@ def test_w4_structured_weights():
     q13 = rng.integers(-8, 8, size=(2 * I, H))
     nib = (q13 & 0xF).astype(np.uint8)
     c13 = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)[None]
-    s13 = np.full((1, 2 * I, H // 128), 2.0 ** -6, np.float32)
+    s13 = np.full((1, H // 128, 2 * I), 2.0 ** -6, np.float32)
     q2 = np.zeros((H, I), np.int64)
     q2[np.arange(H), np.arange(H) % I] = 1
     nib2 = (q2 & 0xF).astype(np.uint8)
     c2 = (nib2[:, 0::2] | (nib2[:, 1::2] << 4)).astype(np.uint8)[None]
-    s2 = np.ones((1, H, I // 128), np.float32)
+    s2 = np.ones((1, I // 128, H), np.float32)
     c = moe.make_config(hidden=H, inter=I, n_experts=E, top_k=1, dtype="w4a16")
     dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(DEV)
     off = torch.tensor([0, T], dtype=torch.int32, device=DEV)

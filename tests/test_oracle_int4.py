@@ -40,17 +40,17 @@ def test_group_scale_mapping():
     # (row, 128-column group), broadcast over the group.
     rows, cols = 3, 384
     packed = np.full((rows, cols // 2), 0x11, np.uint8)
-    s = np.array([[1.0, 2.0, 4.0], [0.5, -3.0, 8.0], [7.0, 0.25, 1.5]], np.float32)
+    s = np.array([[1.0, 2.0, 4.0], [0.5, -3.0, 8.0], [7.0, 0.25, 1.5]], np.float32)   # (group, row)
     w = oracle.dequantize_int4_groups(packed, s)
     for r in range(rows):
         for c in (0, 1, 126, 127, 128, 129, 255, 256, 383):
-            assert w[r, c] == s[r, c // 128]
+            assert w[r, c] == s[c // 128, r]
 
 
 def test_dequantize_is_code_times_scale():
     rng = np.random.default_rng(5)
     packed = rng.integers(0, 256, size=(4, 128), dtype=np.uint8)        # 256 columns
-    s = rng.standard_normal((4, 2)).astype(np.float32)
+    s = rng.standard_normal((2, 4)).astype(np.float32)
     w = oracle.dequantize_int4_groups(packed, s)
     for r in range(4):
         for j in range(128):
@@ -58,7 +58,7 @@ def test_dequantize_is_code_times_scale():
             for half, c in ((0, 2 * j), (1, 2 * j + 1)):
                 n = (byte >> (4 * half)) & 0xF
                 q = n - 16 if n >= 8 else n
-                assert w[r, c] == q * float(s[r, c // 128])
+                assert w[r, c] == q * float(s[c // 128, r])
 
 
 def test_generator_rounding_rule():
@@ -70,12 +70,12 @@ def test_generator_rounding_rule():
     w[2, 128:256] = 0.0
     packed, scales = int4_group_quantize(w)
     assert packed.shape == (5, 256) and packed.dtype == torch.uint8
-    assert scales.shape == (5, 4) and scales.dtype == torch.float32
+    assert scales.shape == (4, 5) and scales.dtype == torch.float32
     q = oracle.unpack_int4(packed.numpy())
     deq = oracle.dequantize_int4_groups(packed.numpy(), scales.numpy())
-    s = np.repeat(scales.numpy().astype(np.float64), 128, axis=1)
+    s = np.repeat(scales.numpy().T.astype(np.float64), 128, axis=1)
     assert np.all(np.abs(deq - w.double().numpy()) <= 0.5 * s * (1 + 1e-6))
     assert q.min() >= -7 and q.max() <= 7
-    gq = np.abs(q.reshape(5, 4, 128)).max(axis=-1)
-    assert np.all(gq[np.arange(5)[:, None], np.arange(4)[None, :]][scales.numpy() != 1.0] == 7)
-    assert scales[2, 1].item() == 1.0 and np.all(q[2, 128:256] == 0)
+    gq = np.abs(q.reshape(5, 4, 128)).max(axis=-1)                 # (row, group)
+    assert np.all(gq[scales.numpy().T != 1.0] == 7)
+    assert scales[1, 2].item() == 1.0 and np.all(q[2, 128:256] == 0)
