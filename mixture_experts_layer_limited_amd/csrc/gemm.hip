@@ -232,13 +232,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets, int E, int bm,
                                                             int ntn, int4* __restrict__ tiles,
                                                             int* __restrict__ n_tiles) {
-  __shared__ int scan[1024];
+  __shared__ int scan[1024];   // inclusive prefix sum of the m-tile counts
+  __shared__ int first[1025];  // offsets[0 .. E]
   const int e = threadIdx.x;
-  int lo = 0, hi = 0, cnt = 0;
+  int cnt = 0;
   if (e < E) {
-    lo = offsets[e];
-    hi = offsets[e + 1];
+    const int lo = offsets[e], hi = offsets[e + 1];
     cnt = (hi - lo + bm - 1) / bm;
+    first[e] = lo;
+    if (e == E - 1) first[E] = hi;
   }
   scan[e] = cnt;
   __syncthreads();
@@ -248,13 +250,24 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     scan[e] += v;
     __syncthreads();
   }
-  const int base = (scan[e] - cnt) * ntn;
-  const int n = hi - lo;
-  for (int nt = 0; nt < ntn; ++nt)
-    for (int i = 0; i < cnt; ++i)
-      tiles[base + nt * cnt + i] =
-          make_int4(e, lo + (int)((int64_t)i * n / cnt), lo + (int)((int64_t)(i + 1) * n / cnt), nt);
-  if (e == 1023) *n_tiles = scan[1023] * ntn;
+  // Entries are written by all threads: entry idx belongs to the expert x
+  // with scan[x - 1] * ntn <= idx < scan[x] * ntn (found by bisection).
+  const int total = scan[1023] * ntn;
+  for (int idx = e; idx < total; idx += 1024) {
+    int lo = 0, hi = E - 1;  // smallest x with scan[x] * ntn > idx
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (scan[mid] * ntn > idx) hi = mid;
+      else lo = mid + 1;
+    }
+    const int x = lo;
+    const int c = scan[x] - (x > 0 ? scan[x - 1] : 0);
+    const int local = idx - (scan[x] - c) * ntn;
+    const int nt = local / c, i = local - nt * c;
+    const int r0 = first[x], n = first[x + 1] - r0;
+    tiles[idx] = make_int4(x, r0 + (int)((int64_t)i * n / c), r0 + (int)((int64_t)(i + 1) * n / c), nt);
+  }
+  if (e == 0) *n_tiles = total;
 }
 
 // ---------------------------------------------------------------- launch ---

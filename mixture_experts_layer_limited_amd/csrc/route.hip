@@ -34,16 +34,18 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(RouteParams p) 
     s[i] = valid[i] ? row[e] : 0.0f;
   }
   // logits of a split-K router GEMM: partial sums of K slices, added in slice
-  // order (loads issued 8 slices at a time)
-  for (int q0 = 1; q0 < p.n_parts; q0 += 8) {
-    float part[8][V];
+  // order; the loads of up to NP slices are in flight at once (about 112
+  // registers), so a decode batch's 50-odd slices take two round trips
+  constexpr int NP = 112 / V < 32 ? (112 / V > 0 ? 112 / V : 1) : 32;
+  for (int q0 = 1; q0 < p.n_parts; q0 += NP) {
+    float part[NP][V];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < NP; ++u)
 #pragma unroll
       for (int i = 0; i < V; ++i)
         part[u][i] = (valid[i] && q0 + u < p.n_parts) ? row[(int64_t)(q0 + u) * p.part_stride + lane * V + i] : 0.0f;
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < NP; ++u)
 #pragma unroll
       for (int i = 0; i < V; ++i)
         if (q0 + u < p.n_parts) s[i] += part[u][i];
