@@ -39,6 +39,8 @@
 //     w / 4 of every step; the two waves of a column group share a SIMD,
 //     where one's MFMAs overlap the other's code widening, and add their sums
 //     through LDS at the end of each tile.
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 #include "lds_dma.h"
@@ -394,6 +396,24 @@ __global__ __launch_bounds__(512, 1) void gemm_w4_kernel(GemmW4Params p) {
 #undef MOE_W4_ISSUE_B
 }
 
+// Compute units of the current device, queried once per device (64 devices at most are remembered).
+static hipError_t device_cus(int* cus) {
+  static std::atomic<int> known[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64) {
+    const int v = known[dev].load(std::memory_order_relaxed);
+    if (v > 0) {
+      *cus = v;
+      return hipSuccess;
+    }
+  }
+  e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess && dev >= 0 && dev < 64) known[dev].store(*cus, std::memory_order_relaxed);
+  return e;
+}
+
 template <int SA, int SB, int EPI, int ODT>
 static hipError_t launch_w4(const GemmW4Params& p, int grid_m, hipStream_t s) {
   constexpr int BN = 256;
@@ -406,9 +426,7 @@ static hipError_t launch_w4(const GemmW4Params& p, int grid_m, hipStream_t s) {
   // one persistent work-group per CU (LDS holds one), at most one per tile
   int cus = 0;
   {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const hipError_t e = device_cus(&cus);
     if (e != hipSuccess) return e;
   }
   const int64_t tiles = (int64_t)grid_m * p.ntn;
