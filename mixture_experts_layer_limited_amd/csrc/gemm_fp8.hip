@@ -433,62 +433,89 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_fp8_split_kernel(GemmFp8
 // One K step: every LDS read of the step (both sub-steps' fragments and the
 // activation scales) first, so none of them follows a ring DMA in program order;
 // then A's ring DMAs with the first sub-step's MFMAs, B's with the second's and
-// the scaled fold of the partials.
+// the scaled fold of the partials.  The fold (two VALU operations per
+// accumulator and 128-wide K block) costs about as long as the block's MFMAs,
+// and the two waves of a SIMD (rows wm = 0 and wm = 1 of one column group)
+// leave each step's barrier together.  So the wm = 1 waves run the loop
+// rotated (ROT): they fold step kt - 1's partials right after step kt's
+// barrier, while their SIMD partner runs step kt's MFMAs, and run their own
+// MFMAs while the partner folds.  The partials and scales of step kt - 1 stay
+// in the same registers across the back edge; no extra registers are needed.
+#define MOE_F8_FOLD()                                                                                \
+  _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                     \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                   \
+      _Pragma("unroll") for (int e = 0; e < 16; ++e)                                                 \
+        acc[i][j][e] += part[i][j][e] * (sa[i][e] * sbk[j])
 #define MOE_F8_KLOOP                                                                                 \
-  for (int kt = 0; kt < nk; ++kt) {                                                                  \
-    wait_vm_barrier<VMN>();                                                                          \
-    const char* sa_ = lds + (kt % SA) * ASLOT;                                                       \
-    const char* sb_ = lds + SA * ASLOT + (kt % SB) * BSLOT;                                          \
-    float sbk[TN];                                                                                   \
-    _Pragma("unroll") for (int j = 0; j < TN; ++j) sbk[j] = sbn[j];                                  \
-    {                                                                                                \
-      const int kn_ = kt + 1 < nk ? kt + 1 : kt;                                                     \
-      _Pragma("unroll") for (int j = 0; j < TN; ++j) sbn[j] = SBg[(int64_t)sbrow[j] * nkb + kn_];    \
-    }                                                                                                \
-    u32x4 a[2][NL][2], b[2][TN][2];                                                                  \
-    MOE_F8_READ(0);                                                                                  \
-    MOE_F8_READ(1);                                                                                  \
-    /* this step's activation scales: rows 8*(e/4) + 4*hi + (e%4) of each block */                  \
-    float sa[NL][16];                                                                                \
-    _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                   \
-      _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                                \
-        const int r_ = (wm + WM * i) * 32 + 8 * q + 4 * hi;                                           \
-        /* read as u32x4 like the fragments (no wait on the ring DMAs in flight) */                \
-        const u32x4 u_ = *(const u32x4*)(sa_ + ADATA + ((r_ / RW) * 64 + r_ % RW) * 4);             \
-        const float4 v_ = __builtin_bit_cast(float4, u_);                                            \
-        sa[i][4 * q + 0] = v_.x; sa[i][4 * q + 1] = v_.y; sa[i][4 * q + 2] = v_.z; sa[i][4 * q + 3] = v_.w; \
-      }                                                                                              \
-    __builtin_amdgcn_sched_barrier(0);                                                               \
-    MOE_F8_ISSUE_A(kt + SA - 1, 0, AI, true);                                                        \
+  {                                                                                                  \
     f32x16 part[NL][TN];                                                                             \
-    _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                   \
-      _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                               \
-        f32x16 z_;                                                                                   \
-        _Pragma("unroll") for (int e = 0; e < 16; ++e) z_[e] = 0.0f;                                 \
-        part[i][j] = mma_fp8(a[0][i][0], a[0][i][1], b[0][j][0], b[0][j][1], z_);                    \
+    float sa[NL][16], sbk[TN];                                                                       \
+    for (int kt = 0; kt < nk; ++kt) {                                                                \
+      wait_vm_barrier<VMN>();                                                                        \
+      const char* sa_ = lds + (kt % SA) * ASLOT;                                                     \
+      const char* sb_ = lds + SA * ASLOT + (kt % SB) * BSLOT;                                        \
+      float sbc[TN];                                                                                 \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j) sbc[j] = sbn[j];                                \
+      {                                                                                              \
+        const int kn_ = kt + 1 < nk ? kt + 1 : kt;                                                   \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j) sbn[j] = SBg[(int64_t)sbrow[j] * nkb + kn_];  \
       }                                                                                              \
-    sub_schedule<0, NL * TN, 0, AL>();                                                               \
-    __builtin_amdgcn_sched_barrier(0);                                                               \
-    MOE_F8_ISSUE_B(kt + SB - 1, 0, BI);                                                              \
-    _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                   \
-      _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                 \
-        part[i][j] = mma_fp8(a[1][i][0], a[1][i][1], b[1][j][0], b[1][j][1], part[i][j]);            \
-    sub_schedule<0, NL * TN, 0, BI>();                                                               \
-    _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                   \
-      _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                 \
-        _Pragma("unroll") for (int e = 0; e < 16; ++e)                                               \
-          acc[i][j][e] += part[i][j][e] * (sa[i][e] * sbk[j]);                                       \
+      u32x4 a[2][NL][2], b[2][TN][2];                                                                \
+      MOE_F8_READ(0);                                                                                \
+      MOE_F8_READ(1);                                                                                \
+      if (ROT && kt > 0) MOE_F8_FOLD();                                                              \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j) sbk[j] = sbc[j];                                \
+      /* this step's activation scales: rows 8*(e/4) + 4*hi + (e%4) of each block */                \
+      _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                 \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                              \
+          const int r_ = (wm + WM * i) * 32 + 8 * q + 4 * hi;                                         \
+          /* read as u32x4 like the fragments (no wait on the ring DMAs in flight) */              \
+          const u32x4 u_ = *(const u32x4*)(sa_ + ADATA + ((r_ / RW) * 64 + r_ % RW) * 4);           \
+          const float4 v_ = __builtin_bit_cast(float4, u_);                                          \
+          sa[i][4 * q + 0] = v_.x; sa[i][4 * q + 1] = v_.y; sa[i][4 * q + 2] = v_.z; sa[i][4 * q + 3] = v_.w; \
+        }                                                                                            \
+      __builtin_amdgcn_sched_barrier(0);                                                             \
+      MOE_F8_ISSUE_A(kt + SA - 1, 0, AI, true);                                                      \
+      _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                 \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                             \
+          f32x16 z_;                                                                                 \
+          _Pragma("unroll") for (int e = 0; e < 16; ++e) z_[e] = 0.0f;                               \
+          part[i][j] = mma_fp8(a[0][i][0], a[0][i][1], b[0][j][0], b[0][j][1], z_);                  \
+        }                                                                                            \
+      sub_schedule<0, NL * TN, 0, AL>();                                                             \
+      __builtin_amdgcn_sched_barrier(0);                                                             \
+      MOE_F8_ISSUE_B(kt + SB - 1, 0, BI);                                                            \
+      _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                 \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j)                                               \
+          part[i][j] = mma_fp8(a[1][i][0], a[1][i][1], b[1][j][0], b[1][j][1], part[i][j]);          \
+      sub_schedule<0, NL * TN, 0, BI>();                                                             \
+      if (!ROT) MOE_F8_FOLD();                                                                       \
+    }                                                                                                \
+    if (ROT && nk > 0) MOE_F8_FOLD();                                                                \
   }
 
   if (tm_live <= 1) {
     constexpr int NL = 1;
-    MOE_F8_KLOOP
+    if (wm == 1) {
+      constexpr bool ROT = true;
+      MOE_F8_KLOOP
+    } else {
+      constexpr bool ROT = false;
+      MOE_F8_KLOOP
+    }
   } else {
     constexpr int NL = TM;
-    MOE_F8_KLOOP
+    if (wm == 1) {
+      constexpr bool ROT = true;
+      MOE_F8_KLOOP
+    } else {
+      constexpr bool ROT = false;
+      MOE_F8_KLOOP
+    }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #undef MOE_F8_KLOOP
+#undef MOE_F8_FOLD
 #undef MOE_F8_READ
 #undef MOE_F8_ISSUE_A
 #undef MOE_F8_ISSUE_B

@@ -14,13 +14,14 @@
 
 namespace moe {
 
-constexpr int kRouteWaves = 4;
-
-template <int V>
-__global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(RouteParams p) {
-  __shared__ float cs[kRouteWaves][V * 64];
+// W tokens (waves) per work-group: 1 for small batches, so that the loads
+// of a split-K router's partial logits spread over as many CUs as there are
+// tokens; 4 for large ones.
+template <int V, int W>
+__global__ __launch_bounds__(W * 64) void route_kernel(RouteParams p) {
+  __shared__ float cs[W][V * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * kRouteWaves + wave;
+  const int t = blockIdx.x * W + wave;
   const bool active = t < p.T;
   const int E = p.E;
 
@@ -158,8 +159,12 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(RouteParams p) 
 
 template <int V>
 static hipError_t launch_v(const RouteParams& p, hipStream_t s) {
-  const int grid = (p.T + kRouteWaves - 1) / kRouteWaves;
-  hipLaunchKernelGGL(route_kernel<V>, dim3(grid), dim3(kRouteWaves * 64), 0, s, p);
+  if (p.T <= 2048) {
+    hipLaunchKernelGGL((route_kernel<V, 1>), dim3(p.T), dim3(64), 0, s, p);
+  } else {
+    const int grid = (p.T + 3) / 4;
+    hipLaunchKernelGGL((route_kernel<V, 4>), dim3(grid), dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 
