@@ -339,10 +339,11 @@ __global__ __launch_bounds__(512, 1) void gemm_w4_kernel(GemmW4Params p) {
     // row 4 q + r, column n.  Stores go through a buffer resource over the
     // tile's rows: every store instruction is issued (a fixed count per
     // tile), lanes without an element write out of range and are dropped.
+    // Only the first wave set holds the sums.  (The scatter path's row indices
+    // and weights are vector loads: waiting for them also waits for the ring
+    // DMAs in flight, one drain per tile on that path.)
     const int rows = ct.r1 - ct.r0;
-    if (kset == 1) {
-      // nothing to store
-    } else if constexpr (EPI == EPI_SCATTER) {
+    if (kset == 0 && EPI == EPI_SCATTER) {
       const int col0 = ct.nt * BN;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -357,7 +358,7 @@ __global__ __launch_bounds__(512, 1) void gemm_w4_kernel(GemmW4Params p) {
           if (col < p.N) atomicAdd((float*)p.C + (int64_t)tok * p.N + col, w * acc[jb][r]);
         }
       }
-    } else {
+    } else if (kset == 0) {
       constexpr int EB = EPI == EPI_SWIGLU ? 2 : Elem<ODT>::kBytes;
       const __amdgpu_buffer_rsrc_t rc =
           make_rsrc((const char*)p.C + (int64_t)ct.r0 * p.N * EB, (int64_t)rows * p.N * EB);
