@@ -230,6 +230,9 @@ SMALL = {
                           topk_group=2, top_k=4, shared_inter=128, bias="zero"),
     # 4-bit weights, decode batch with the Zipf-skewed load: many empty and one-row experts
     "w4_decode_like": _reduced("v3_decode_w4a16", hidden=1024, inter=256, shared_inter=256),
+    # 4-bit weights with the largest expert count and top-k: 1024 groups in the tile list
+    "w4_max_experts_top_k": _reduced("v3_decode_w4a16", tokens=150, hidden=256, inter=128, n_experts=1024,
+                                     top_k=32, shared_inter=128, bias="zero"),
     # 4-bit weights at T > 1024: the shared expert of the routed width runs its own dense launches
     "w4_large_t": _reduced("v3_decode_w4a16", tokens=1100, hidden=512, inter=256, n_experts=32, shared_inter=256,
                            bias="zero"),
