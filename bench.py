@@ -194,13 +194,15 @@ def main():
         step()
     ev = HipEvents(4 * a.steps)
     torch.cuda.synchronize()
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_start.record()
+    # one event between consecutive steps: the whole region and every step's own time
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+    marks[0].record()
     for i in range(a.steps):
         step(tuple(ev.ev[4 * i:4 * i + 4]))
-    t_end.record()
+        marks[i + 1].record()
     torch.cuda.synchronize()
-    ms = t_start.elapsed_time(t_end) / a.steps
+    ms = marks[0].elapsed_time(marks[-1]) / a.steps
+    per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(a.steps)])
     g1 = float(np.mean([ev.ms(ev.ev[4 * i], ev.ev[4 * i + 1]) for i in range(a.steps)]))
     g2 = float(np.mean([ev.ms(ev.ev[4 * i + 2], ev.ev[4 * i + 3]) for i in range(a.steps)]))
     ev.close()
@@ -246,6 +248,8 @@ def main():
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": ms,
+        "step_ms": {"median": float(np.median(per_step)), "p10": float(np.percentile(per_step, 10)),
+                    "p90": float(np.percentile(per_step, 90))},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
