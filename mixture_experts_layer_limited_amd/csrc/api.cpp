@@ -347,8 +347,8 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
     const bool dense = offsets == nullptr;
     const int ntn1 = ntiles_n(I, g1.bn / 2), ntn2 = ntiles_n(H, g2.bn);
     if (!dense) {
-      HIP_TRY(launch_build_tiles(offsets, groups, g1.bm, ntn1, w.tiles1, w.ntiles1, s));
-      HIP_TRY(launch_build_tiles(offsets, groups, g2.bm, ntn2, w.tiles2, w.ntiles2, s));
+      HIP_TRY(launch_build_tiles(offsets, groups, g1.bm, ntn1, w.tiles1, w.ntiles1, s, g2.bm, ntn2, w.tiles2,
+                                 w.ntiles2));
     }
     GemmFp8Params p{};
     p.A = xq; p.a_scales = xs; p.a_rows = src;
@@ -397,8 +397,8 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
     const bool dense = offsets == nullptr;
     const int ntn1 = ntiles_n(I, g1.bn / 2), ntn2 = ntiles_n(H, g2.bn);
     if (!dense) {
-      HIP_TRY(launch_build_tiles(offsets, groups, g1.bm, ntn1, w.tiles1, w.ntiles1, s));
-      HIP_TRY(launch_build_tiles(offsets, groups, g2.bm, ntn2, w.tiles2, w.ntiles2, s));
+      HIP_TRY(launch_build_tiles(offsets, groups, g1.bm, ntn1, w.tiles1, w.ntiles1, s, g2.bm, ntn2, w.tiles2,
+                                 w.ntiles2));
     }
     GemmW4Params p{};
     p.A = hidden; p.a_rows = src;
@@ -440,8 +440,8 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
   const bool dense = offsets == nullptr;
   const int ntn1 = ntiles_n(I, g1.bn / 2), ntn2 = ntiles_n(H, g2.bn);
   if (!dense) {
-    HIP_TRY(launch_build_tiles(offsets, groups, g1.bm, ntn1, w.tiles1, w.ntiles1, s));
-    HIP_TRY(launch_build_tiles(offsets, groups, g2.bm, ntn2, w.tiles2, w.ntiles2, s));
+    HIP_TRY(launch_build_tiles(offsets, groups, g1.bm, ntn1, w.tiles1, w.ntiles1, s, g2.bm, ntn2, w.tiles2,
+                               w.ntiles2));
   }
   GemmParams p{};
   p.A = hidden; p.a_rows = src;

@@ -8,9 +8,10 @@
 namespace moe {
 
 // out[t] = acc[t] + sum_j w[t,j] * rows[inv[t*k+j]] + shared[t], fp32 sum in
-// that order, one rounding.  One block per token, 8 consecutive columns per
-// thread per pass, moved with 16-byte loads and stores (H % 8 == 0; row starts
-// are 16-byte aligned for every H the ABI accepts).
+// that order, one rounding.  Block (t, s) covers columns [2048 s, 2048 s + 2048)
+// of token t (so a small batch still spreads over the chip), 8 consecutive
+// columns per thread, moved with 16-byte loads and stores (H % 8 == 0; row
+// starts are 16-byte aligned for every H the ABI accepts).
 template <int ADT>
 __device__ __forceinline__ void load8(const typename Elem<ADT>::T* p, float v[8]) {
   if constexpr (ADT == MOE_DT_BF16) {
@@ -49,6 +50,7 @@ __global__ __launch_bounds__(256) void combine_kernel(int H, int k, const void* 
   __shared__ int pos[32];
   __shared__ float wt[32];
   const int t = blockIdx.x;
+  const int c_end = min(H, (int)(blockIdx.y + 1) * 2048);
   if (expert_out && threadIdx.x < k) {
     pos[threadIdx.x] = inv[(int64_t)t * k + threadIdx.x];
     wt[threadIdx.x] = topk_w[(int64_t)t * k + threadIdx.x];
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(256) void combine_kernel(int H, int k, const void* 
   const T* rows = (const T*)expert_out;
   const T* sh = (const T*)shared_out;
   T* o = (T*)out;
-  for (int c = threadIdx.x * 8; c < H; c += blockDim.x * 8) {
+  for (int c = blockIdx.y * 2048 + threadIdx.x * 8; c < c_end; c += blockDim.x * 8) {
     float v[8];
     if (acc) {
       const float4 a0 = *(const float4*)(acc + (int64_t)t * H + c);
@@ -91,12 +93,13 @@ hipError_t launch_combine(int adt, int T, int H, int k, const void* expert_out, 
                           const int32_t* inv, const float* topk_w, const void* shared_out, void* out,
                           hipStream_t s) {
   if (T <= 0) return hipSuccess;
+  const dim3 grid(T, (H + 2047) / 2048);
   if (adt == MOE_DT_BF16)
-    hipLaunchKernelGGL(combine_kernel<MOE_DT_BF16>, dim3(T), dim3(256), 0, s, H, k, expert_out, acc, inv,
-                       topk_w, shared_out, out);
+    hipLaunchKernelGGL(combine_kernel<MOE_DT_BF16>, grid, dim3(256), 0, s, H, k, expert_out, acc, inv, topk_w,
+                       shared_out, out);
   else
-    hipLaunchKernelGGL(combine_kernel<MOE_DT_F32>, dim3(T), dim3(256), 0, s, H, k, expert_out, acc, inv,
-                       topk_w, shared_out, out);
+    hipLaunchKernelGGL(combine_kernel<MOE_DT_F32>, grid, dim3(256), 0, s, H, k, expert_out, acc, inv, topk_w,
+                       shared_out, out);
   return hipGetLastError();
 }
 

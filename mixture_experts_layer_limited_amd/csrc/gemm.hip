@@ -230,8 +230,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
 // weight tile read it from that XCD's L2 instead of from HBM.
 // Entry: {expert, first row, end row, n-tile}; *n_tiles = sum_e c_e * ntn.
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets, int E, int bm,
-                                                            int ntn, int4* __restrict__ tiles,
-                                                            int* __restrict__ n_tiles) {
+                                                            int ntn, int4* __restrict__ tiles, int* __restrict__ n_tiles,
+                                                            int ntn2, int4* __restrict__ tiles2,
+                                                            int* __restrict__ n_tiles2) {
   __shared__ int scan[1024];   // inclusive prefix sum of the m-tile counts
   __shared__ int first[1025];  // offsets[0 .. E]
   const int e = threadIdx.x;
@@ -251,23 +252,30 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     __syncthreads();
   }
   // Entries are written by all threads: entry idx belongs to the expert x
-  // with scan[x - 1] * ntn <= idx < scan[x] * ntn (found by bisection).
-  const int total = scan[1023] * ntn;
-  for (int idx = e; idx < total; idx += 1024) {
-    int lo = 0, hi = E - 1;  // smallest x with scan[x] * ntn > idx
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (scan[mid] * ntn > idx) hi = mid;
-      else lo = mid + 1;
+  // with scan[x - 1] * ntn <= idx < scan[x] * ntn (found by bisection).  A
+  // second list with the same m-tiles and another n-tile count (ntn2 > 0)
+  // comes from the same scan.
+  for (int list = 0; list < 2; ++list) {
+    const int nn = list ? ntn2 : ntn;
+    int4* out = list ? tiles2 : tiles;
+    if (nn <= 0) break;
+    const int total = scan[1023] * nn;
+    for (int idx = e; idx < total; idx += 1024) {
+      int lo = 0, hi = E - 1;  // smallest x with scan[x] * nn > idx
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (scan[mid] * nn > idx) hi = mid;
+        else lo = mid + 1;
+      }
+      const int x = lo;
+      const int c = scan[x] - (x > 0 ? scan[x - 1] : 0);
+      const int local = idx - (scan[x] - c) * nn;
+      const int nt = local / c, i = local - nt * c;
+      const int r0 = first[x], n = first[x + 1] - r0;
+      out[idx] = make_int4(x, r0 + (int)((int64_t)i * n / c), r0 + (int)((int64_t)(i + 1) * n / c), nt);
     }
-    const int x = lo;
-    const int c = scan[x] - (x > 0 ? scan[x - 1] : 0);
-    const int local = idx - (scan[x] - c) * ntn;
-    const int nt = local / c, i = local - nt * c;
-    const int r0 = first[x], n = first[x + 1] - r0;
-    tiles[idx] = make_int4(x, r0 + (int)((int64_t)i * n / c), r0 + (int)((int64_t)(i + 1) * n / c), nt);
+    if (e == 0) *(list ? n_tiles2 : n_tiles) = total;
   }
-  if (e == 0) *n_tiles = total;
 }
 
 // ---------------------------------------------------------------- launch ---
@@ -367,8 +375,17 @@ hipError_t launch_gemm(int dt, int epi, int odt, const GemmParams& p, const Gemm
 }
 
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int bm, int ntn, int4* tiles, int* n_tiles,
-                              hipStream_t s) {
-  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm, ntn, tiles, n_tiles);
+                              hipStream_t s, int bm2, int ntn2, int4* tiles2, int* n_tiles2) {
+  if (tiles2 && bm2 == bm) {  // both lists from one scan
+    hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm, ntn, tiles, n_tiles, ntn2,
+                       tiles2, n_tiles2);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm, ntn, tiles, n_tiles, 0,
+                     (int4*)nullptr, (int*)nullptr);
+  if (tiles2)
+    hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm2, ntn2, tiles2, n_tiles2, 0,
+                       (int4*)nullptr, (int*)nullptr);
   return hipGetLastError();
 }
 

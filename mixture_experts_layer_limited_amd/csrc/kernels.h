@@ -47,8 +47,11 @@ hipError_t launch_gemm(int dt, int epi, int odt, const GemmParams& p, const Gemm
                        hipStream_t s);
 // Pipelined bf16 kernel (LDS ring filled by direct-to-LDS buffer loads).
 hipError_t launch_gemm_pipe(int epi, int odt, const GemmParams& p, const GemmShape& g, int grid_m, hipStream_t s);
+// The tile list of a grouped GEMM; with tiles2, a second list (another n-tile
+// count) in the same launch when bm2 == bm, else in a launch of its own.
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int bm, int ntn, int4* tiles, int* n_tiles,
-                              hipStream_t s);
+                              hipStream_t s, int bm2 = 0, int ntn2 = 0, int4* tiles2 = nullptr,
+                              int* n_tiles2 = nullptr);
 
 // FP8 grouped GEMM: A = E4M3 codes with 1x128 fp32 scales, B = E4M3 codes with
 // 128x128 fp32 block scales.
