@@ -648,9 +648,9 @@ int moe_forward(const moe_config* c, int64_t T, const void* hidden, const void* 
   const int64_t rows_all = rows + (merged ? T : 0);
 
   MOE_TRY(do_route(c, T, hidden, gate_w, bias, nullptr, scores, ids, topw, w.route.logits, stream));
-  HIP_TRY(launch_permute(ids, (int)rows, c->top_k, E, w.perm.counts, offsets, src, inv, stream));
+  HIP_TRY(launch_permute(ids, (int)rows, c->top_k, E, w.perm.counts, offsets, src, inv, stream,
+                         merged ? (int)T : 0));
   if (merged) {
-    HIP_TRY(launch_extend_shared(offsets, E, (int)rows, (int)T, src, stream));
     if (opts && opts->expert_offsets)
       HIP_TRY(hipMemcpyAsync(opts->expert_offsets, offsets, (size_t)(E + 1) * sizeof(int32_t),
                              hipMemcpyDeviceToDevice, stream));

@@ -125,8 +125,10 @@ struct RouteParams {
 };
 hipError_t launch_route(const RouteParams& p, hipStream_t s);
 
+// ext_T > 0: also offsets[E+1] = n + ext_T and src[n + t] = t (the shared
+// expert as group E).
 hipError_t launch_permute(const int32_t* ids, int n, int k, int E, int32_t* counts, int32_t* offsets,
-                          int32_t* src, int32_t* inv, hipStream_t s);
+                          int32_t* src, int32_t* inv, hipStream_t s, int ext_T = 0);
 int permute_blocks(int n);
 // offsets[E+1] = rows + T and src[rows + t] = t: the shared expert as group E.
 hipError_t launch_extend_shared(int32_t* offsets, int E, int rows, int T, int32_t* src, hipStream_t s);

@@ -101,14 +101,86 @@ __global__ __launch_bounds__(64) void perm_scatter(const int32_t* __restrict__ i
   }
 }
 
+// Small batches (n <= kSmallPermute copies): the whole permutation in one
+// work-group, one launch instead of three: an LDS histogram, the scan, then
+// wave 0 places the copies in order with the ballot ranking of perm_scatter
+// (the same stable result); with ext_T > 0 also the shared expert as group E.
+constexpr int kSmallPermute = 4096;
+
+__global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ ids, int n, int k, int E,
+                                                   int32_t* __restrict__ offsets, int32_t* __restrict__ src,
+                                                   int32_t* __restrict__ inv, int ext_T) {
+  __shared__ int run[1024];  // counts, then the next free slot of each expert
+  __shared__ int scan[1024];
+  const int tid = threadIdx.x;
+  run[tid] = 0;
+  __syncthreads();
+  for (int a = tid; a < n; a += 1024) atomicAdd(&run[min(max(ids[a], 0), E - 1)], 1);
+  __syncthreads();
+  const int cnt = tid < E ? run[tid] : 0;
+  scan[tid] = cnt;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = tid >= o ? scan[tid - o] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  const int excl = scan[tid] - cnt;
+  if (tid < E) {
+    offsets[tid] = excl;
+    run[tid] = excl;
+  }
+  if (tid == E - 1) offsets[E] = excl + cnt;
+  __syncthreads();
+  if (tid < 64) {
+    const int lane = tid;
+    int bits = 0;
+    while ((1 << bits) < E) ++bits;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int g = 0; g < n; g += 64) {
+      const int a = g + lane;
+      const bool ok = a < n;
+      const int e = ok ? min(max(ids[a], 0), E - 1) : 0;
+      uint64_t same = __ballot(ok);
+      for (int b = 0; b < bits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t bal = __ballot(bit);
+        same &= bit ? bal : ~bal;
+      }
+      const int rank = __popcll(same & lt);
+      const int pos = run[e] + rank;
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): every lane has read run[] before it changes
+      __builtin_amdgcn_wave_barrier();
+      if (ok && rank == 0) run[e] = pos + __popcll(same);
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+      if (ok) {
+        src[pos] = a / k;
+        inv[a] = pos;
+      }
+    }
+  }
+  if (ext_T > 0) {
+    for (int t = tid; t < ext_T; t += 1024) src[n + t] = t;
+    if (tid == 0) offsets[E + 1] = n + ext_T;
+  }
+}
+
 hipError_t launch_permute(const int32_t* ids, int n, int k, int E, int32_t* counts, int32_t* offsets,
-                          int32_t* src, int32_t* inv, hipStream_t s) {
+                          int32_t* src, int32_t* inv, hipStream_t s, int ext_T) {
+  if (n <= 0) return hipSuccess;
+  if (n <= kSmallPermute) {
+    hipLaunchKernelGGL(perm_small, dim3(1), dim3(1024), 0, s, ids, n, k, E, offsets, src, inv, ext_T);
+    return hipGetLastError();
+  }
   const int nb = permute_blocks(n);
-  if (nb == 0) return hipSuccess;
   hipLaunchKernelGGL(perm_hist, dim3(nb), dim3(256), 0, s, ids, n, E, counts);
   hipLaunchKernelGGL(perm_scan, dim3(1), dim3(1024), 0, s, counts, nb, E, offsets);
   hipLaunchKernelGGL(perm_scatter, dim3(nb), dim3(64), 0, s, ids, n, k, E, counts, src, inv);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ext_T <= 0) return e;
+  return launch_extend_shared(offsets, E, n, ext_T, src, s);
 }
 
 }  // namespace moe

@@ -155,6 +155,7 @@ def test_permute_walkthrough_example():
     (1, 8, 2, "random"), (61, 8, 2, "random"), (4096, 64, 6, "random"), (8192, 256, 8, "random"),
     (16384, 256, 8, "random"), (777, 1024, 32, "random"), (3000, 64, 6, "one"), (128, 256, 8, "skew"),
     (129, 3, 2, "random"),
+    (512, 64, 8, "random"), (513, 64, 8, "random"),   # 4096 copies (one work-group) and just past it
 ])
 def test_permute_bit_exact(T, E, k, mode):
     say(f"permute T={T} E={E} k={k} {mode}")
