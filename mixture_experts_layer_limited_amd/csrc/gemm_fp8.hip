@@ -446,50 +446,69 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_fp8_split_kernel(GemmFp8
     _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                   \
       _Pragma("unroll") for (int e = 0; e < 16; ++e)                                                 \
         acc[i][j][e] += part[i][j][e] * (sa[i][e] * sbk[j])
+// Step kt = kt0 + OFF_ of the K loop, in ring slot SLOT_ (= kt % SA = kt % SB).
+// Unrolled by the ring depth, the slot is a compile-time constant and the
+// per-lane LDS addresses of each slot are loop invariant.
+#define MOE_F8_STEP(OFF_, SLOT_)                                                                     \
+  if (kt0 + (OFF_) < nk) {                                                                           \
+    const int kt = kt0 + (OFF_);                                                                     \
+    wait_vm_barrier<VMN>();                                                                          \
+    const char* sa_ = lds + (SLOT_) * ASLOT;                                                         \
+    const char* sb_ = lds + SA * ASLOT + (SLOT_) * BSLOT;                                            \
+    float sbc[TN];                                                                                   \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j) sbc[j] = sbn[j];                                  \
+    {                                                                                                \
+      const int kn_ = kt + 1 < nk ? kt + 1 : kt;                                                     \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j) sbn[j] = SBg[(int64_t)sbrow[j] * nkb + kn_];    \
+    }                                                                                                \
+    u32x4 a[2][NL][2], b[2][TN][2];                                                                  \
+    MOE_F8_READ(0);                                                                                  \
+    MOE_F8_READ(1);                                                                                  \
+    if (ROT && kt > 0) MOE_F8_FOLD();                                                                \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j) sbk[j] = sbc[j];                                  \
+    /* this step's activation scales: rows 8*(e/4) + 4*hi + (e%4) of each block */                  \
+    _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                   \
+      _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                                \
+        const int r_ = (wm + WM * i) * 32 + 8 * q + 4 * hi;                                           \
+        /* read as u32x4 like the fragments (no wait on the ring DMAs in flight) */                \
+        const u32x4 u_ = *(const u32x4*)(sa_ + ADATA + ((r_ / RW) * 64 + r_ % RW) * 4);             \
+        const float4 v_ = __builtin_bit_cast(float4, u_);                                            \
+        sa[i][4 * q + 0] = v_.x; sa[i][4 * q + 1] = v_.y; sa[i][4 * q + 2] = v_.z; sa[i][4 * q + 3] = v_.w; \
+      }                                                                                              \
+    __builtin_amdgcn_sched_barrier(0);                                                               \
+    MOE_F8_ISSUE_A(kt + SA - 1, 0, AI, true);                                                        \
+    _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                   \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                               \
+        f32x16 z_;                                                                                   \
+        _Pragma("unroll") for (int e = 0; e < 16; ++e) z_[e] = 0.0f;                                 \
+        part[i][j] = mma_fp8(a[0][i][0], a[0][i][1], b[0][j][0], b[0][j][1], z_);                    \
+      }                                                                                              \
+    sub_schedule<0, NL * TN, 0, AL>();                                                               \
+    __builtin_amdgcn_sched_barrier(0);                                                               \
+    MOE_F8_ISSUE_B(kt + SB - 1, 0, BI);                                                              \
+    _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                   \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                 \
+        part[i][j] = mma_fp8(a[1][i][0], a[1][i][1], b[1][j][0], b[1][j][1], part[i][j]);            \
+    sub_schedule<0, NL * TN, 0, BI>();                                                               \
+    if (!ROT) MOE_F8_FOLD();                                                                         \
+  }
+// The SwiGLU instance needs more address registers (gate and up blocks) than
+// the unrolled loop leaves, so it keeps the rolled loop (slot kt % 3 at run time).
 #define MOE_F8_KLOOP                                                                                 \
   {                                                                                                  \
+    static_assert(SA == SB && SA == 3, "the unrolled K loop walks both rings' 3 slots together");    \
     f32x16 part[NL][TN];                                                                             \
     float sa[NL][16], sbk[TN];                                                                       \
-    for (int kt = 0; kt < nk; ++kt) {                                                                \
-      wait_vm_barrier<VMN>();                                                                        \
-      const char* sa_ = lds + (kt % SA) * ASLOT;                                                     \
-      const char* sb_ = lds + SA * ASLOT + (kt % SB) * BSLOT;                                        \
-      float sbc[TN];                                                                                 \
-      _Pragma("unroll") for (int j = 0; j < TN; ++j) sbc[j] = sbn[j];                                \
-      {                                                                                              \
-        const int kn_ = kt + 1 < nk ? kt + 1 : kt;                                                   \
-        _Pragma("unroll") for (int j = 0; j < TN; ++j) sbn[j] = SBg[(int64_t)sbrow[j] * nkb + kn_];  \
+    if constexpr (EPI == EPI_SWIGLU) {                                                               \
+      for (int kt0 = 0; kt0 < nk; ++kt0) {                                                           \
+        MOE_F8_STEP(0, kt0 % 3)                                                                      \
       }                                                                                              \
-      u32x4 a[2][NL][2], b[2][TN][2];                                                                \
-      MOE_F8_READ(0);                                                                                \
-      MOE_F8_READ(1);                                                                                \
-      if (ROT && kt > 0) MOE_F8_FOLD();                                                              \
-      _Pragma("unroll") for (int j = 0; j < TN; ++j) sbk[j] = sbc[j];                                \
-      /* this step's activation scales: rows 8*(e/4) + 4*hi + (e%4) of each block */                \
-      _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                 \
-        _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                              \
-          const int r_ = (wm + WM * i) * 32 + 8 * q + 4 * hi;                                         \
-          /* read as u32x4 like the fragments (no wait on the ring DMAs in flight) */              \
-          const u32x4 u_ = *(const u32x4*)(sa_ + ADATA + ((r_ / RW) * 64 + r_ % RW) * 4);           \
-          const float4 v_ = __builtin_bit_cast(float4, u_);                                          \
-          sa[i][4 * q + 0] = v_.x; sa[i][4 * q + 1] = v_.y; sa[i][4 * q + 2] = v_.z; sa[i][4 * q + 3] = v_.w; \
-        }                                                                                            \
-      __builtin_amdgcn_sched_barrier(0);                                                             \
-      MOE_F8_ISSUE_A(kt + SA - 1, 0, AI, true);                                                      \
-      _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                 \
-        _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                             \
-          f32x16 z_;                                                                                 \
-          _Pragma("unroll") for (int e = 0; e < 16; ++e) z_[e] = 0.0f;                               \
-          part[i][j] = mma_fp8(a[0][i][0], a[0][i][1], b[0][j][0], b[0][j][1], z_);                  \
-        }                                                                                            \
-      sub_schedule<0, NL * TN, 0, AL>();                                                             \
-      __builtin_amdgcn_sched_barrier(0);                                                             \
-      MOE_F8_ISSUE_B(kt + SB - 1, 0, BI);                                                            \
-      _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                 \
-        _Pragma("unroll") for (int j = 0; j < TN; ++j)                                               \
-          part[i][j] = mma_fp8(a[1][i][0], a[1][i][1], b[1][j][0], b[1][j][1], part[i][j]);          \
-      sub_schedule<0, NL * TN, 0, BI>();                                                             \
-      if (!ROT) MOE_F8_FOLD();                                                                       \
+    } else {                                                                                         \
+      for (int kt0 = 0; kt0 < nk; kt0 += 3) {                                                        \
+        MOE_F8_STEP(0, 0)                                                                            \
+        MOE_F8_STEP(1, 1)                                                                            \
+        MOE_F8_STEP(2, 2)                                                                            \
+      }                                                                                              \
     }                                                                                                \
     if (ROT && nk > 0) MOE_F8_FOLD();                                                                \
   }
@@ -515,6 +534,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_fp8_split_kernel(GemmFp8
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #undef MOE_F8_KLOOP
+#undef MOE_F8_STEP
 #undef MOE_F8_FOLD
 #undef MOE_F8_READ
 #undef MOE_F8_ISSUE_A
