@@ -244,7 +244,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_kernel(GemmFp8Params p)
 // carries the step's activation scales of the tile's rows (one 4-byte DMA lane
 // per row).  Weight-block scales are wave-uniform scalar loads, fetched one step
 // ahead.  Per step and 32x32 block: two 32x32x64 MFMAs into a zeroed partial,
-// then acc += partial * (sa[row] * sb).
+// then acc += partial * (sa[row] * sb); the SwiGLU and row-store instances run
+// each block transposed so that one scale product serves a lane's 16 results.
 template <int WM, int WN, int TM, int TN, int SA, int SB, int EPI>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_fp8_split_kernel(GemmFp8Params p) {
   constexpr int NW = WM * WN;
@@ -263,6 +264,13 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_fp8_split_kernel(GemmFp8
   static_assert(RW == 16 || RW == 32 || RW == 64, "scale rows per wave");
   static_assert(SA >= 2 && SB >= SA && VMN < 64, "ring depths");
   static_assert(EPI != EPI_SWIGLU || TN % 2 == 0, "SwiGLU pairs gate and up tiles");
+  // The SwiGLU and row-store instances compute each 32x32 block transposed
+  // (weight rows as the MFMA's first operand): a lane's 16 results then share
+  // one token and one weight block, so the fold takes one scale product per
+  // block and one FMA per accumulator instead of two operations per
+  // accumulator.  The scatter instance keeps token rows first, so that its
+  // fp32 atomics cover 32 consecutive columns per row.
+  constexpr bool TR = EPI != EPI_SCATTER;
 
   extern __shared__ __attribute__((aligned(16))) char lds[];
   lds_char* const lds3 = (lds_char*)lds;
@@ -443,9 +451,15 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_fp8_split_kernel(GemmFp8
 // in the same registers across the back edge; no extra registers are needed.
 #define MOE_F8_FOLD()                                                                                \
   _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                     \
-    _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                   \
-      _Pragma("unroll") for (int e = 0; e < 16; ++e)                                                 \
-        acc[i][j][e] += part[i][j][e] * (sa[i][e] * sbk[j])
+    _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                                 \
+      if constexpr (TR) {                                                                            \
+        const float s_ = sa[i][0] * sbk[j];                                                          \
+        _Pragma("unroll") for (int e = 0; e < 16; ++e) acc[i][j][e] += part[i][j][e] * s_;          \
+      } else {                                                                                       \
+        _Pragma("unroll") for (int e = 0; e < 16; ++e)                                               \
+          acc[i][j][e] += part[i][j][e] * (sa[i][e] * sbk[j]);                                       \
+      }                                                                                              \
+    }
 // Step kt = kt0 + OFF_ of the K loop, in ring slot SLOT_ (= kt % SA = kt % SB).
 // Unrolled by the ring depth, the slot is a compile-time constant and the
 // per-lane LDS addresses of each slot are loop invariant.
@@ -466,49 +480,50 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_fp8_split_kernel(GemmFp8
     MOE_F8_READ(1);                                                                                  \
     if (ROT && kt > 0) MOE_F8_FOLD();                                                                \
     _Pragma("unroll") for (int j = 0; j < TN; ++j) sbk[j] = sbc[j];                                  \
-    /* this step's activation scales: rows 8*(e/4) + 4*hi + (e%4) of each block */                  \
-    _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                   \
-      _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                                \
-        const int r_ = (wm + WM * i) * 32 + 8 * q + 4 * hi;                                           \
-        /* read as u32x4 like the fragments (no wait on the ring DMAs in flight) */                \
-        const u32x4 u_ = *(const u32x4*)(sa_ + ADATA + ((r_ / RW) * 64 + r_ % RW) * 4);             \
-        const float4 v_ = __builtin_bit_cast(float4, u_);                                            \
-        sa[i][4 * q + 0] = v_.x; sa[i][4 * q + 1] = v_.y; sa[i][4 * q + 2] = v_.z; sa[i][4 * q + 3] = v_.w; \
+    /* this step's activation scales: transposed, the lane's token (row lr of each */               \
+    /* block); else rows 8*(e/4) + 4*hi + (e%4) of each block */                                     \
+    _Pragma("unroll") for (int i = 0; i < NL; ++i) {                                                 \
+      if constexpr (TR) {                                                                            \
+        const int r_ = (wm + WM * i) * 32 + lr;                                                      \
+        sa[i][0] = __builtin_bit_cast(float, *(const uint32_t*)(sa_ + ADATA + ((r_ / RW) * 64 + r_ % RW) * 4)); \
+      } else {                                                                                       \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                              \
+          const int r_ = (wm + WM * i) * 32 + 8 * q + 4 * hi;                                         \
+          /* read as u32x4 like the fragments (no wait on the ring DMAs in flight) */              \
+          const u32x4 u_ = *(const u32x4*)(sa_ + ADATA + ((r_ / RW) * 64 + r_ % RW) * 4);           \
+          const float4 v_ = __builtin_bit_cast(float4, u_);                                          \
+          sa[i][4 * q + 0] = v_.x; sa[i][4 * q + 1] = v_.y; sa[i][4 * q + 2] = v_.z; sa[i][4 * q + 3] = v_.w; \
+        }                                                                                            \
       }                                                                                              \
+    }                                                                                                \
     __builtin_amdgcn_sched_barrier(0);                                                               \
     MOE_F8_ISSUE_A(kt + SA - 1, 0, AI, true);                                                        \
     _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                   \
       _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                               \
         f32x16 z_;                                                                                   \
         _Pragma("unroll") for (int e = 0; e < 16; ++e) z_[e] = 0.0f;                                 \
-        part[i][j] = mma_fp8(a[0][i][0], a[0][i][1], b[0][j][0], b[0][j][1], z_);                    \
+        part[i][j] = TR ? mma_fp8(b[0][j][0], b[0][j][1], a[0][i][0], a[0][i][1], z_)                \
+                        : mma_fp8(a[0][i][0], a[0][i][1], b[0][j][0], b[0][j][1], z_);               \
       }                                                                                              \
     sub_schedule<0, NL * TN, 0, AL>();                                                               \
     __builtin_amdgcn_sched_barrier(0);                                                               \
     MOE_F8_ISSUE_B(kt + SB - 1, 0, BI);                                                              \
     _Pragma("unroll") for (int i = 0; i < NL; ++i)                                                   \
       _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                 \
-        part[i][j] = mma_fp8(a[1][i][0], a[1][i][1], b[1][j][0], b[1][j][1], part[i][j]);            \
+        part[i][j] = TR ? mma_fp8(b[1][j][0], b[1][j][1], a[1][i][0], a[1][i][1], part[i][j])        \
+                        : mma_fp8(a[1][i][0], a[1][i][1], b[1][j][0], b[1][j][1], part[i][j]);       \
     sub_schedule<0, NL * TN, 0, BI>();                                                               \
     if (!ROT) MOE_F8_FOLD();                                                                         \
   }
-// The SwiGLU instance needs more address registers (gate and up blocks) than
-// the unrolled loop leaves, so it keeps the rolled loop (slot kt % 3 at run time).
 #define MOE_F8_KLOOP                                                                                 \
   {                                                                                                  \
     static_assert(SA == SB && SA == 3, "the unrolled K loop walks both rings' 3 slots together");    \
     f32x16 part[NL][TN];                                                                             \
-    float sa[NL][16], sbk[TN];                                                                       \
-    if constexpr (EPI == EPI_SWIGLU) {                                                               \
-      for (int kt0 = 0; kt0 < nk; ++kt0) {                                                           \
-        MOE_F8_STEP(0, kt0 % 3)                                                                      \
-      }                                                                                              \
-    } else {                                                                                         \
-      for (int kt0 = 0; kt0 < nk; kt0 += 3) {                                                        \
-        MOE_F8_STEP(0, 0)                                                                            \
-        MOE_F8_STEP(1, 1)                                                                            \
-        MOE_F8_STEP(2, 2)                                                                            \
-      }                                                                                              \
+    float sa[NL][TR ? 1 : 16], sbk[TN];                                                              \
+    for (int kt0 = 0; kt0 < nk; kt0 += 3) {                                                          \
+      MOE_F8_STEP(0, 0)                                                                              \
+      MOE_F8_STEP(1, 1)                                                                              \
+      MOE_F8_STEP(2, 2)                                                                              \
     }                                                                                                \
     if (ROT && nk > 0) MOE_F8_FOLD();                                                                \
   }
@@ -549,28 +564,28 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_fp8_split_kernel(GemmFp8
     constexpr int RB = OC * 2 + 16;
     constexpr int JO = EPI == EPI_SWIGLU ? TN / 2 : TN;
     static_assert(BM * RB <= SA * ASLOT + SB * BSLOT, "staging fits the rings");
-    const bool odd = lr & 1;
+    static_assert(TR, "the staged epilogue reads transposed blocks");
     __syncthreads();
+    // Transposed blocks: lane (lr, hi) holds token row lr of the block and
+    // columns 8q + 4hi .. 8q + 4hi + 3 in results 4q .. 4q + 3: one 8-byte LDS
+    // write per q.
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       if (i >= tm_live) continue;
+      const int row = (wm + WM * i) * 32 + lr;
 #pragma unroll
       for (int jo = 0; jo < JO; ++jo) {
-        const int c = (EPI == EPI_SWIGLU ? wn * (TN / 2) + jo : bblock(jo)) * 32 + lr;
+        const int cb = (EPI == EPI_SWIGLU ? wn * (TN / 2) + jo : bblock(jo)) * 32 + 4 * hi;
 #pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-          float v0, v1;
-          if constexpr (EPI == EPI_SWIGLU) {
-            v0 = silu_mul8(acc[i][jo][e], acc[i][jo + TN / 2][e]);
-            v1 = silu_mul8(acc[i][jo][e + 1], acc[i][jo + TN / 2][e + 1]);
-          } else {
-            v0 = acc[i][jo][e];
-            v1 = acc[i][jo][e + 1];
+        for (int q = 0; q < 4; ++q) {
+          float v[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if constexpr (EPI == EPI_SWIGLU) v[u] = silu_mul8(acc[i][jo][4 * q + u], acc[i][jo + TN / 2][4 * q + u]);
+            else v[u] = acc[i][jo][4 * q + u];
           }
-          const float recv = swap_adjacent_lanes(odd ? v0 : v1);
-          const int row = (wm + WM * i) * 32 + 8 * (e >> 2) + 4 * hi + (e & 3) + (odd ? 1 : 0);
-          const int col = odd ? c - 1 : c;
-          *(uint32_t*)(lds + row * RB + 2 * col) = odd ? pack_bf16_rne(recv, v1) : pack_bf16_rne(v0, recv);
+          const uint2 w2 = {pack_bf16_rne(v[0], v[1]), pack_bf16_rne(v[2], v[3])};
+          *(uint2*)(lds + row * RB + 2 * (cb + 8 * q)) = w2;
         }
       }
     }
