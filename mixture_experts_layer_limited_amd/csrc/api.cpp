@@ -191,7 +191,8 @@ void carve_swiglu(Carver& cv, const moe_config* c, int64_t T, int64_t rows, int 
   w.tiles2 = cv.take<int4>((size_t)max_mtiles(rows, g2.bm, groups) * ntiles_n(c->hidden, g2.bn) + 1);
   w.ntiles2 = cv.take<int>(1);
   if (is_fp8(c)) {
-    w.h = cv.take<uint16_t>((size_t)rows * I);
+    // the pipelined gate/up kernel writes h already quantised; the register-staged one writes bf16 h
+    w.h = g1.kind == 1 ? nullptr : cv.take<uint16_t>((size_t)rows * I);
     w.hq = cv.take<uint8_t>((size_t)rows * I);
     w.h_scales = cv.take<float>((size_t)rows * (I / 128));
     if (quantize_x) {
@@ -360,7 +361,12 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
     p.b_gstride = (int64_t)2 * I * H; p.bs_gstride = (int64_t)(2 * I / 128) * (H / 128);
     if (sg) { p.B2 = (const uint8_t*)sg->w13; p.b2_scales = sg->w13_s; p.b2_group = sg->group; }
     p.K = H; p.N = I;
-    p.C = w.h;
+    const int64_t hst = g2.kind == 1 ? rows : 0;  // k-block-major h scales for the pipelined kernel
+    if (g1.kind == 1) {  // the pipelined kernel quantises h in its epilogue
+      p.Cq = w.hq; p.Cs = w.h_scales; p.cs_stride = hst;
+    } else {
+      p.C = w.h;
+    }
     p.a_nrows = T;
     set_tiles(p, dense, rows, g1.bm, w.tiles1, w.ntiles1);
     p.ntn = ntn1;
@@ -368,8 +374,7 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
     MOE_TRY(mark(0));
     HIP_TRY(launch_gemm_fp8(EPI_SWIGLU, p, g1, gm1, s));
     MOE_TRY(mark(1));
-    const int64_t hst = g2.kind == 1 ? rows : 0;  // k-block-major h scales for the pipelined kernel
-    HIP_TRY(launch_quantize(MOE_DT_BF16, rows, I, w.h, w.hq, w.h_scales, s, hst));
+    if (g1.kind != 1) HIP_TRY(launch_quantize(MOE_DT_BF16, rows, I, w.h, w.hq, w.h_scales, s, hst));
     GemmFp8Params q{};
     q.A = w.hq; q.a_scales = w.h_scales; q.a_rows = nullptr; q.as_stride = hst;
     q.B = (const uint8_t*)w2; q.b_scales = w2_s;

@@ -169,12 +169,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(int64_t rows, int64_t col
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
   const float scale = m > 0.0f ? m / 448.0f : 1.0f;
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    lo |= f32_to_e4m3(v[q] / scale) << (8 * q);
-    hi |= f32_to_e4m3(v[q + 4] / scale) << (8 * q);
-  }
+  const uint32_t lo = e4m3x4(v[0] / scale, v[1] / scale, v[2] / scale, v[3] / scale);
+  const uint32_t hi = e4m3x4(v[4] / scale, v[5] / scale, v[6] / scale, v[7] / scale);
   *(uint2*)(codes + base) = make_uint2(lo, hi);
   if (sub == 0) {
     if (st_stride > 0) scales[(c0 / 128) * st_stride + r] = scale;  // k-block-major

@@ -555,43 +555,96 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_fp8_split_kernel(GemmFp8
 #undef MOE_F8_ISSUE_A
 #undef MOE_F8_ISSUE_B
 
-  if constexpr (EPI == EPI_STORE || EPI == EPI_SWIGLU) {
-    // bf16 tile through LDS (the rings are idle now) and 16-byte row stores; lanes
-    // l and l^1 trade one value per row pair so each lane writes a dword of two
-    // adjacent columns (even lanes row r, columns c, c+1; odd lanes row r+1,
-    // columns c-1, c).  Rows are padded by 16 bytes.
-    constexpr int OC = EPI == EPI_SWIGLU ? BN / 2 : BN;
-    constexpr int RB = OC * 2 + 16;
-    constexpr int JO = EPI == EPI_SWIGLU ? TN / 2 : TN;
+  if constexpr (EPI == EPI_SWIGLU) {
+    // h = SiLU(g) * u leaves as E4M3 codes with their 1x128 scales (the
+    // activation rule of the down GEMM's input): the tile's 128 output columns
+    // are exactly one scale block of each row.  Per row, the amax meets over the
+    // lane pair (hi) and the WN waves of the row (through LDS); then the codes go
+    // through LDS to 16-byte row stores.  h is quantised from its fp32 value.
+    constexpr int OC = BN / 2;
+    constexpr int JO = TN / 2;
+    constexpr int RQ = OC + 16;                        // LDS bytes per staged row of codes
+    static_assert(OC == 128, "one 1x128 scale block per tile row");
+    static_assert(TR, "the epilogue reads transposed blocks");
+    static_assert(BM * RQ + BM * WN * 4 <= SA * ASLOT + SB * BSLOT, "staging fits the rings");
+    float* const amax_l = (float*)(lds + BM * RQ);     // [BM][WN] per-wave row maxima
+    __syncthreads();
+    float hv[TM][JO][16];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if (i >= tm_live) continue;
+      float m = 0.0f;
+#pragma unroll
+      for (int jo = 0; jo < JO; ++jo)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          hv[i][jo][e] = silu_mul8(acc[i][jo][e], acc[i][jo + TN / 2][e]);
+          m = fmaxf(m, fabsf(hv[i][jo][e]));
+        }
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      if (hi == 0) amax_l[((wm + WM * i) * 32 + lr) * WN + wn] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if (i >= tm_live) continue;
+      const int row = (wm + WM * i) * 32 + lr;
+      float m = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WN; ++w) m = fmaxf(m, amax_l[row * WN + w]);
+      const float scale = m > 0.0f ? m / 448.0f : 1.0f;
+#pragma unroll
+      for (int jo = 0; jo < JO; ++jo) {
+        const int cb = (wn * (TN / 2) + jo) * 32 + 4 * hi;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          *(uint32_t*)(lds + row * RQ + cb + 8 * q) =
+              e4m3x4(hv[i][jo][4 * q] / scale, hv[i][jo][4 * q + 1] / scale, hv[i][jo][4 * q + 2] / scale,
+                     hv[i][jo][4 * q + 3] / scale);
+        }
+      }
+      if (wn == 0 && hi == 0 && row < rows) {
+        if (p.cs_stride > 0) p.Cs[(int64_t)nt * p.cs_stride + r0 + row] = scale;  // k-block-major
+        else p.Cs[(int64_t)(r0 + row) * (p.N / 128) + nt] = scale;
+      }
+    }
+    __syncthreads();
+    constexpr int CPRq = OC / 16;
+    for (int q = tid; q < BM * CPRq; q += NW * 64) {
+      const int row = q / CPRq, ch = q % CPRq;
+      if (row < rows)
+        *(u32x4*)(p.Cq + (int64_t)(r0 + row) * p.N + nt * OC + ch * 16) = *(const u32x4*)(lds + row * RQ + ch * 16);
+    }
+    return;
+  }
+
+  if constexpr (EPI == EPI_STORE) {
+    // bf16 tile through LDS (the rings are idle now) and 16-byte row stores.
+    // Rows are padded by 16 bytes.  Transposed blocks: lane (lr, hi) holds token
+    // row lr of the block and columns 8q + 4hi .. 8q + 4hi + 3 in results
+    // 4q .. 4q + 3, one 8-byte LDS write per q.
+    constexpr int RB = BN * 2 + 16;
     static_assert(BM * RB <= SA * ASLOT + SB * BSLOT, "staging fits the rings");
     static_assert(TR, "the staged epilogue reads transposed blocks");
     __syncthreads();
-    // Transposed blocks: lane (lr, hi) holds token row lr of the block and
-    // columns 8q + 4hi .. 8q + 4hi + 3 in results 4q .. 4q + 3: one 8-byte LDS
-    // write per q.
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       if (i >= tm_live) continue;
       const int row = (wm + WM * i) * 32 + lr;
 #pragma unroll
-      for (int jo = 0; jo < JO; ++jo) {
-        const int cb = (EPI == EPI_SWIGLU ? wn * (TN / 2) + jo : bblock(jo)) * 32 + 4 * hi;
+      for (int j = 0; j < TN; ++j) {
+        const int cb = bblock(j) * 32 + 4 * hi;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          float v[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            if constexpr (EPI == EPI_SWIGLU) v[u] = silu_mul8(acc[i][jo][4 * q + u], acc[i][jo + TN / 2][4 * q + u]);
-            else v[u] = acc[i][jo][4 * q + u];
-          }
-          const uint2 w2 = {pack_bf16_rne(v[0], v[1]), pack_bf16_rne(v[2], v[3])};
+          const uint2 w2 = {pack_bf16_rne(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                            pack_bf16_rne(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
           *(uint2*)(lds + row * RB + 2 * (cb + 8 * q)) = w2;
         }
       }
     }
     __syncthreads();
-    constexpr int CPRo = OC / 8;
-    const int c0 = nt * OC;
+    constexpr int CPRo = BN / 8;
+    const int c0 = nt * BN;
     for (int q = tid; q < BM * CPRo; q += NW * 64) {
       const int row = q / CPRo, ch = q % CPRo;
       const int col = c0 + ch * 8;
@@ -687,6 +740,7 @@ static hipError_t launch8(const GemmFp8Params& p, int grid_m, hipStream_t s) {
 
 hipError_t launch_gemm_fp8(int epi, const GemmFp8Params& p, const GemmShape& g, int grid_m, hipStream_t s) {
   if (g.kind == 1) {
+    if (epi == EPI_SWIGLU && (!p.Cq || !p.Cs)) return hipErrorInvalidValue;  // writes quantised h only
     switch (epi) {
       case EPI_SWIGLU: return launch8_split<2, 4, 2, 2, 3, 3, EPI_SWIGLU>(p, grid_m, s);
       case EPI_SCATTER: return launch8_split<2, 4, 2, 2, 3, 3, EPI_SCATTER>(p, grid_m, s);

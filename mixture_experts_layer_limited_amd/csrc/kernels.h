@@ -69,7 +69,10 @@ struct GemmFp8Params {
   int b2_group;
   int K;
   int N;
-  void* C;                // SwiGLU: bf16 h [rows, N]; store: bf16 [rows, N]; scatter: fp32 [T, N]
+  void* C;                // SwiGLU (kind 0): bf16 h [rows, N]; store: bf16 [rows, N]; scatter: fp32 [T, N]
+  uint8_t* Cq;            // SwiGLU (kind 1): E4M3 codes of h [rows, N] ...
+  float* Cs;              // ... and their 1x128 scales: Cs[kb * cs_stride + row] when cs_stride > 0,
+  int64_t cs_stride;      //     else Cs[row * (N / 128) + kb]
   const int32_t* c_rows;
   const float* row_w;
   const int4* tiles;

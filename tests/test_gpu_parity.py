@@ -197,6 +197,38 @@ def test_quantize_bit_exact(rows, cols, dt):
     assert np.array_equal(got, rc), f"{(got != rc).sum()} codes differ"
 
 
+def test_quantize_every_code_and_midpoint():
+    """Every E4M3 value, every midpoint between neighbours and the fp32 values
+    two ulps around each, both signs, through the 1x128 quantiser: each tile
+    holds 448 so its scale is exactly 1 and the codes are the rounding rule's
+    own, compared bit for bit with the oracle's encoder."""
+    pos = np.unique(oracle.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8)).astype(np.float64))
+    pts = np.concatenate([pos, (pos[1:] + pos[:-1]) / 2]).astype(np.float32)
+    vals = [pts]
+    for _ in range(2):
+        vals.append(np.nextafter(vals[-1], np.float32(np.inf)))
+    vals.append(np.nextafter(pts, np.float32(-np.inf)))
+    vals.append(np.nextafter(vals[-1], np.float32(-np.inf)))
+    v = np.concatenate(vals)
+    v = v[(v >= 0) & (v <= 448)]
+    v = np.concatenate([v, -v]).astype(np.float32)
+    n_tiles = -(-v.size // 127)
+    x = np.zeros((n_tiles, 128), np.float32)
+    x[:, 0] = 448.0
+    flat = x[:, 1:].reshape(-1)
+    flat[:v.size] = v
+    x[:, 1:] = flat.reshape(n_tiles, 127)
+    say(f"quantize every code: {v.size} values in {n_tiles} tiles")
+    codes = torch.empty(n_tiles, 128, dtype=torch.uint8, device=DEV)
+    scales = f32((n_tiles, 1))
+    moe.quantize_fp8_1x128(torch.from_numpy(x).to(DEV), codes, scales)
+    torch.cuda.synchronize()
+    rc, rs = oracle.quantize_1x128(x)
+    assert np.all(rs == 1.0)
+    got = codes.cpu().numpy()
+    assert np.array_equal(got, rc), f"{(got != rc).sum()} codes differ"
+
+
 # -------------------------------------------------- grouped SwiGLU + combine ---
 
 def _reduced(name, **kw):
