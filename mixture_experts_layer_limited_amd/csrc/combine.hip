@@ -71,20 +71,12 @@ __global__ __launch_bounds__(256) void combine_kernel(int H, int k, const void* 
       for (int i = 0; i < 8; ++i) v[i] = 0.0f;
     }
     if (rows) {
-      // the loads of up to 8 expert rows go out together, then add in j order
-      for (int j0 = 0; j0 < k; j0 += 8) {
-        float r[8][8];
+      for (int j = 0; j < k; ++j) {
+        float r[8];
+        load8<ADT>(rows + (int64_t)pos[j] * H + c, r);
+        const float w = wt[j];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-          if (j0 + jj < k) load8<ADT>(rows + (int64_t)pos[j0 + jj] * H + c, r[jj]);
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          if (j0 + jj < k) {
-            const float w = wt[j0 + jj];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] += w * r[jj][i];
-          }
-        }
+        for (int i = 0; i < 8; ++i) v[i] += w * r[i];
       }
     }
     if (sh) {
