@@ -329,7 +329,7 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
               const float* hidden_scales, const int32_t* src, const int32_t* offsets, const void* w13,
               const float* w13_s, const void* w2, const float* w2_s, int epi, const float* topk_w,
               const int32_t* inv, void* out, float* acc, const SwigluWs& w, hipStream_t s,
-              hipEvent_t const* ev = nullptr, const SharedGroup* sg = nullptr) {
+              hipEvent_t const* ev = nullptr, const SharedGroup* sg = nullptr, bool tiles_ready = false) {
   auto mark = [&](int i) -> int {
     if (ev && ev[i]) return hip_status(hipEventRecord(ev[i], s));
     return MOE_OK;
@@ -347,7 +347,7 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
     const GemmShape g2 = fp8_shape2(c, rows, groups, I);
     const bool dense = offsets == nullptr;
     const int ntn1 = ntiles_n(I, g1.bn / 2), ntn2 = ntiles_n(H, g2.bn);
-    if (!dense) {
+    if (!dense && !tiles_ready) {
       HIP_TRY(launch_build_tiles(offsets, groups, g1.bm, ntn1, w.tiles1, w.ntiles1, s, g2.bm, ntn2, w.tiles2,
                                  w.ntiles2));
     }
@@ -401,7 +401,7 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
     const GemmShape g1 = gemm_w4_shape(), g2 = gemm_w4_shape();
     const bool dense = offsets == nullptr;
     const int ntn1 = ntiles_n(I, g1.bn / 2), ntn2 = ntiles_n(H, g2.bn);
-    if (!dense) {
+    if (!dense && !tiles_ready) {
       HIP_TRY(launch_build_tiles(offsets, groups, g1.bm, ntn1, w.tiles1, w.ntiles1, s, g2.bm, ntn2, w.tiles2,
                                  w.ntiles2));
     }
@@ -444,7 +444,7 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
   const GemmShape g2 = shape2(c, rows, groups, I);
   const bool dense = offsets == nullptr;
   const int ntn1 = ntiles_n(I, g1.bn / 2), ntn2 = ntiles_n(H, g2.bn);
-  if (!dense) {
+  if (!dense && !tiles_ready) {
     HIP_TRY(launch_build_tiles(offsets, groups, g1.bm, ntn1, w.tiles1, w.ntiles1, s, g2.bm, ntn2, w.tiles2,
                                w.ntiles2));
   }
@@ -653,8 +653,20 @@ int moe_forward(const moe_config* c, int64_t T, const void* hidden, const void* 
   const int64_t rows_all = rows + (merged ? T : 0);
 
   MOE_TRY(do_route(c, T, hidden, gate_w, bias, nullptr, scores, ids, topw, w.route.logits, stream));
+  // Small batches: the permutation's one work-group also writes both GEMMs' tile
+  // lists (when their m-tiles have one height).
+  const int groups = E + (merged ? 1 : 0);
+  const GemmShape g1 = tile_shape1(c, T, rows_all, groups, c->inter);
+  const GemmShape g2 = tile_shape2(c, rows_all, groups, c->inter);
+  TileLists tl;
+  if (g1.bm == g2.bm) {
+    tl.bm = g1.bm;
+    tl.ntn = ntiles_n(c->inter, g1.bn / 2); tl.tiles = w.routed.tiles1; tl.n_tiles = w.routed.ntiles1;
+    tl.ntn2 = ntiles_n(c->hidden, g2.bn); tl.tiles2 = w.routed.tiles2; tl.n_tiles2 = w.routed.ntiles2;
+  }
+  bool tiles_ready = false;
   HIP_TRY(launch_permute(ids, (int)rows, c->top_k, E, w.perm.counts, offsets, src, inv, stream,
-                         merged ? (int)T : 0));
+                         merged ? (int)T : 0, tl.bm > 0 ? &tl : nullptr, &tiles_ready));
   if (merged) {
     if (opts && opts->expert_offsets)
       HIP_TRY(hipMemcpyAsync(opts->expert_offsets, offsets, (size_t)(E + 1) * sizeof(int32_t),
@@ -680,9 +692,9 @@ int moe_forward(const moe_config* c, int64_t T, const void* hidden, const void* 
   }
   if (scatter) HIP_TRY(launch_fill_zero(w.acc, T * c->hidden, stream));
   const SharedGroup sg{sh_w13, sh_w13_scales, sh_w2, sh_w2_scales, E};
-  MOE_TRY(do_swiglu(c, T, rows_all, E + (merged ? 1 : 0), c->inter, xin, xs, src, offsets, w13, w13_scales, w2,
-                    w2_scales, epi, topw, inv, w.y, w.acc, w.routed, stream, opts ? opts->events : nullptr,
-                    merged ? &sg : nullptr));
+  MOE_TRY(do_swiglu(c, T, rows_all, groups, c->inter, xin, xs, src, offsets, w13, w13_scales, w2, w2_scales, epi,
+                    topw, inv, w.y, w.acc, w.routed, stream, opts ? opts->events : nullptr, merged ? &sg : nullptr,
+                    tiles_ready));
   const void* shared_rows = merged ? (const void*)((const char*)w.y + rows * c->hidden * act_bytes(c)) : w.sh_out;
   HIP_TRY(launch_combine(act_dt(c), (int)T, c->hidden, c->top_k, w.y, w.acc, inv, topw, shared_rows, out, stream));
   return MOE_OK;

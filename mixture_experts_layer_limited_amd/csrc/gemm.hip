@@ -15,6 +15,7 @@
 // count and surplus work-groups exit at once.
 #include "common.h"
 #include "kernels.h"
+#include "tiles.h"
 #include "lds_dma.h"
 
 namespace moe {
@@ -222,60 +223,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
 
 // ------------------------------------------------------------ m-tile list ---
 
-// One block: the tile list of a grouped GEMM.  Expert e's rows are split into
-// c_e = ceil(rows / bm) m-tiles of near-equal size; the list holds every
-// (m-tile, n-tile) pair, expert by expert, n-tile by n-tile, with the c_e
-// m-tiles of one n-tile next to each other.  Neighbouring entries run at the
-// same time on the same XCD (see xcd_remap), so the m-tiles that share a
-// weight tile read it from that XCD's L2 instead of from HBM.
-// Entry: {expert, first row, end row, n-tile}; *n_tiles = sum_e c_e * ntn.
-__global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets, int E, int bm,
-                                                            int ntn, int4* __restrict__ tiles, int* __restrict__ n_tiles,
-                                                            int ntn2, int4* __restrict__ tiles2,
-                                                            int* __restrict__ n_tiles2) {
-  __shared__ int scan[1024];   // inclusive prefix sum of the m-tile counts
+// One block: the tile lists of a grouped GEMM pair (write_tile_lists).
+__global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets, int E, TileLists t) {
+  __shared__ int scan[1024];
   __shared__ int first[1025];  // offsets[0 .. E]
   const int e = threadIdx.x;
-  int cnt = 0;
   if (e < E) {
-    const int lo = offsets[e], hi = offsets[e + 1];
-    cnt = (hi - lo + bm - 1) / bm;
-    first[e] = lo;
-    if (e == E - 1) first[E] = hi;
+    first[e] = offsets[e];
+    if (e == E - 1) first[E] = offsets[E];
   }
-  scan[e] = cnt;
   __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int v = e >= o ? scan[e - o] : 0;
-    __syncthreads();
-    scan[e] += v;
-    __syncthreads();
-  }
-  // Entries are written by all threads: entry idx belongs to the expert x
-  // with scan[x - 1] * ntn <= idx < scan[x] * ntn (found by bisection).  A
-  // second list with the same m-tiles and another n-tile count (ntn2 > 0)
-  // comes from the same scan.
-  for (int list = 0; list < 2; ++list) {
-    const int nn = list ? ntn2 : ntn;
-    int4* out = list ? tiles2 : tiles;
-    if (nn <= 0) break;
-    const int total = scan[1023] * nn;
-    for (int idx = e; idx < total; idx += 1024) {
-      int lo = 0, hi = E - 1;  // smallest x with scan[x] * nn > idx
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (scan[mid] * nn > idx) hi = mid;
-        else lo = mid + 1;
-      }
-      const int x = lo;
-      const int c = scan[x] - (x > 0 ? scan[x - 1] : 0);
-      const int local = idx - (scan[x] - c) * nn;
-      const int nt = local / c, i = local - nt * c;
-      const int r0 = first[x], n = first[x + 1] - r0;
-      out[idx] = make_int4(x, r0 + (int)((int64_t)i * n / c), r0 + (int)((int64_t)(i + 1) * n / c), nt);
-    }
-    if (e == 0) *(list ? n_tiles2 : n_tiles) = total;
-  }
+  write_tile_lists(scan, first, E, t);
 }
 
 // ---------------------------------------------------------------- launch ---
@@ -376,16 +334,19 @@ hipError_t launch_gemm(int dt, int epi, int odt, const GemmParams& p, const Gemm
 
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int bm, int ntn, int4* tiles, int* n_tiles,
                               hipStream_t s, int bm2, int ntn2, int4* tiles2, int* n_tiles2) {
+  TileLists t;
+  t.bm = bm; t.ntn = ntn; t.tiles = tiles; t.n_tiles = n_tiles;
   if (tiles2 && bm2 == bm) {  // both lists from one scan
-    hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm, ntn, tiles, n_tiles, ntn2,
-                       tiles2, n_tiles2);
+    t.ntn2 = ntn2; t.tiles2 = tiles2; t.n_tiles2 = n_tiles2;
+    hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, t);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm, ntn, tiles, n_tiles, 0,
-                     (int4*)nullptr, (int*)nullptr);
-  if (tiles2)
-    hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm2, ntn2, tiles2, n_tiles2, 0,
-                       (int4*)nullptr, (int*)nullptr);
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, t);
+  if (tiles2) {
+    TileLists t2;
+    t2.bm = bm2; t2.ntn = ntn2; t2.tiles = tiles2; t2.n_tiles = n_tiles2;
+    hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, E, t2);
+  }
   return hipGetLastError();
 }
 

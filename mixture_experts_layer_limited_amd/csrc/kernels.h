@@ -49,6 +49,17 @@ hipError_t launch_gemm(int dt, int epi, int odt, const GemmParams& p, const Gemm
 hipError_t launch_gemm_pipe(int epi, int odt, const GemmParams& p, const GemmShape& g, int grid_m, hipStream_t s);
 // The tile list of a grouped GEMM; with tiles2, a second list (another n-tile
 // count) in the same launch when bm2 == bm, else in a launch of its own.
+// Where the tile lists of a grouped GEMM pair go: m-tiles of bm rows, ntn
+// n-tiles in the first list and ntn2 (0: none) in the second.
+struct TileLists {
+  int bm = 0;
+  int ntn = 0;
+  int4* tiles = nullptr;
+  int* n_tiles = nullptr;
+  int ntn2 = 0;
+  int4* tiles2 = nullptr;
+  int* n_tiles2 = nullptr;
+};
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int bm, int ntn, int4* tiles, int* n_tiles,
                               hipStream_t s, int bm2 = 0, int ntn2 = 0, int4* tiles2 = nullptr,
                               int* n_tiles2 = nullptr);
@@ -130,8 +141,12 @@ hipError_t launch_route(const RouteParams& p, hipStream_t s);
 
 // ext_T > 0: also offsets[E+1] = n + ext_T and src[n + t] = t (the shared
 // expert as group E).
+// tl (optional): the GEMMs' tile lists over the E (+1 with ext_T) groups, also
+// written when the batch is small enough for the one-work-group permutation;
+// *tiles_done tells whether they were.
 hipError_t launch_permute(const int32_t* ids, int n, int k, int E, int32_t* counts, int32_t* offsets,
-                          int32_t* src, int32_t* inv, hipStream_t s, int ext_T = 0);
+                          int32_t* src, int32_t* inv, hipStream_t s, int ext_T = 0, const TileLists* tl = nullptr,
+                          bool* tiles_done = nullptr);
 int permute_blocks(int n);
 // offsets[E+1] = rows + T and src[rows + t] = t: the shared expert as group E.
 hipError_t launch_extend_shared(int32_t* offsets, int E, int rows, int T, int32_t* src, hipStream_t s);

@@ -12,6 +12,7 @@
 //                    a position).
 #include "common.h"
 #include "kernels.h"
+#include "tiles.h"
 
 namespace moe {
 
@@ -105,13 +106,15 @@ __global__ __launch_bounds__(64) void perm_scatter(const int32_t* __restrict__ i
 // work-group, one launch instead of three: an LDS histogram, the scan, then
 // wave 0 places the copies in order with the ballot ranking of perm_scatter
 // (the same stable result); with ext_T > 0 also the shared expert as group E.
+// With t.bm > 0 the same work-group writes the GEMMs' tile lists as well.
 constexpr int kSmallPermute = 4096;
 
 __global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ ids, int n, int k, int E,
                                                    int32_t* __restrict__ offsets, int32_t* __restrict__ src,
-                                                   int32_t* __restrict__ inv, int ext_T) {
+                                                   int32_t* __restrict__ inv, int ext_T, TileLists t) {
   __shared__ int run[1024];  // counts, then the next free slot of each expert
   __shared__ int scan[1024];
+  __shared__ int first[1026];  // the groups' first rows (tile lists)
   const int tid = threadIdx.x;
   run[tid] = 0;
   __syncthreads();
@@ -130,9 +133,15 @@ __global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ i
   if (tid < E) {
     offsets[tid] = excl;
     run[tid] = excl;
+    first[tid] = excl;
   }
-  if (tid == E - 1) offsets[E] = excl + cnt;
+  if (tid == E - 1) {
+    offsets[E] = excl + cnt;
+    first[E] = n;
+    first[E + 1] = n + ext_T;
+  }
   __syncthreads();
+  if (t.bm > 0) write_tile_lists(scan, first, ext_T > 0 ? E + 1 : E, t);
   if (tid < 64) {
     const int lane = tid;
     int bits = 0;
@@ -168,11 +177,16 @@ __global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ i
 }
 
 hipError_t launch_permute(const int32_t* ids, int n, int k, int E, int32_t* counts, int32_t* offsets,
-                          int32_t* src, int32_t* inv, hipStream_t s, int ext_T) {
+                          int32_t* src, int32_t* inv, hipStream_t s, int ext_T, const TileLists* tl,
+                          bool* tiles_done) {
+  if (tiles_done) *tiles_done = false;
   if (n <= 0) return hipSuccess;
   if (n <= kSmallPermute) {
-    hipLaunchKernelGGL(perm_small, dim3(1), dim3(1024), 0, s, ids, n, k, E, offsets, src, inv, ext_T);
-    return hipGetLastError();
+    const TileLists t = (tl && E + (ext_T > 0 ? 1 : 0) <= 1024) ? *tl : TileLists{};
+    hipLaunchKernelGGL(perm_small, dim3(1), dim3(1024), 0, s, ids, n, k, E, offsets, src, inv, ext_T, t);
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess && tiles_done) *tiles_done = t.bm > 0;
+    return e;
   }
   const int nb = permute_blocks(n);
   hipLaunchKernelGGL(perm_hist, dim3(nb), dim3(256), 0, s, ids, n, E, counts);

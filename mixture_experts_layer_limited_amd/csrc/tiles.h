@@ -1,0 +1,55 @@
+// Tile lists of the grouped GEMMs, written by one work-group of 1024 threads
+// (the tile-list kernel, and the one-work-group permutation of small batches).
+#pragma once
+
+#include "kernels.h"
+
+namespace moe {
+
+// Group g's rows are [first[g], first[g + 1]), g < G <= 1024; both arrays in
+// LDS, scan has 1024 entries and every thread of the block must call.  Group g
+// is split into c_g = ceil(rows / bm) m-tiles of near-equal size; a list holds
+// every (m-tile, n-tile) pair, group by group, n-tile by n-tile, with the c_g
+// m-tiles of one n-tile next to each other.  Neighbouring entries run at the
+// same time on the same XCD (see xcd_remap), so the m-tiles that share a
+// weight tile read it from that XCD's L2 instead of from HBM.
+// Entry: {group, first row, end row, n-tile}; *n_tiles = sum_g c_g * ntn.  A
+// second list with the same m-tiles and another n-tile count (ntn2 > 0) comes
+// from the same scan.
+__device__ inline void write_tile_lists(int* scan, const int* first, int G, const TileLists& t) {
+  const int e = threadIdx.x;
+  const int cnt = e < G ? (first[e + 1] - first[e] + t.bm - 1) / t.bm : 0;
+  scan[e] = cnt;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = e >= o ? scan[e - o] : 0;
+    __syncthreads();
+    scan[e] += v;
+    __syncthreads();
+  }
+  // entry idx belongs to the group x with scan[x - 1] * nn <= idx < scan[x] * nn
+  // (found by bisection)
+  for (int list = 0; list < 2; ++list) {
+    const int nn = list ? t.ntn2 : t.ntn;
+    int4* out = list ? t.tiles2 : t.tiles;
+    if (nn <= 0) break;
+    const int total = scan[1023] * nn;
+    for (int idx = e; idx < total; idx += 1024) {
+      int lo = 0, hi = G - 1;  // smallest x with scan[x] * nn > idx
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (scan[mid] * nn > idx) hi = mid;
+        else lo = mid + 1;
+      }
+      const int x = lo;
+      const int c = scan[x] - (x > 0 ? scan[x - 1] : 0);
+      const int local = idx - (scan[x] - c) * nn;
+      const int nt = local / c, i = local - nt * c;
+      const int r0 = first[x], n = first[x + 1] - r0;
+      out[idx] = make_int4(x, r0 + (int)((int64_t)i * n / c), r0 + (int)((int64_t)(i + 1) * n / c), nt);
+    }
+    if (e == 0) *(list ? t.n_tiles2 : t.n_tiles) = total;
+  }
+}
+
+}  // namespace moe
