@@ -39,13 +39,25 @@ __global__ __launch_bounds__(256) void perm_hist(const int32_t* __restrict__ ids
 
 // One block of 1024 threads, thread e owns expert e (E <= 1024).  Rewrites
 // counts[b][e] in place into the first permuted slot of chunk b for expert e.
+// With t.bm > 0 it also writes the GEMMs' tile lists over the E groups (E + 1
+// with the shared expert's ext_T rows as group E).
 __global__ __launch_bounds__(1024) void perm_scan(int32_t* __restrict__ counts, int nb, int E,
-                                                  int32_t* __restrict__ offsets) {
+                                                  int32_t* __restrict__ offsets, int ext_T, TileLists t) {
   __shared__ int scan[1024];
+  __shared__ int first[1026];
   const int e = threadIdx.x;
   int total = 0;
-  if (e < E)
-    for (int b = 0; b < nb; ++b) total += counts[(int64_t)b * E + e];
+  if (e < E) {  // 8 chunks' counts in flight at a time
+    int b = 0;
+    for (; b + 8 <= nb; b += 8) {
+      int c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = counts[(int64_t)(b + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) total += c[u];
+    }
+    for (; b < nb; ++b) total += counts[(int64_t)b * E + e];
+  }
   scan[e] = total;
   __syncthreads();
   for (int o = 1; o < 1024; o <<= 1) {
@@ -57,14 +69,34 @@ __global__ __launch_bounds__(1024) void perm_scan(int32_t* __restrict__ counts, 
   const int excl = scan[e] - total;
   if (e < E) {
     offsets[e] = excl;
+    first[e] = excl;
     int run = excl;
-    for (int b = 0; b < nb; ++b) {
+    int b = 0;
+    for (; b + 8 <= nb; b += 8) {
+      int c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = counts[(int64_t)(b + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        counts[(int64_t)(b + u) * E + e] = run;
+        run += c[u];
+      }
+    }
+    for (; b < nb; ++b) {
       const int c = counts[(int64_t)b * E + e];
       counts[(int64_t)b * E + e] = run;
       run += c;
     }
   }
-  if (e == E - 1) offsets[E] = excl + total;
+  if (e == E - 1) {
+    offsets[E] = excl + total;
+    first[E] = excl + total;
+    first[E + 1] = excl + total + ext_T;
+  }
+  if (t.bm > 0) {
+    __syncthreads();
+    write_tile_lists(scan, first, ext_T > 0 ? E + 1 : E, t);
+  }
 }
 
 __global__ __launch_bounds__(64) void perm_scatter(const int32_t* __restrict__ ids, int n, int k, int E,
@@ -189,10 +221,12 @@ hipError_t launch_permute(const int32_t* ids, int n, int k, int E, int32_t* coun
     return e;
   }
   const int nb = permute_blocks(n);
+  const TileLists t = (tl && E + (ext_T > 0 ? 1 : 0) <= 1024) ? *tl : TileLists{};
   hipLaunchKernelGGL(perm_hist, dim3(nb), dim3(256), 0, s, ids, n, E, counts);
-  hipLaunchKernelGGL(perm_scan, dim3(1), dim3(1024), 0, s, counts, nb, E, offsets);
+  hipLaunchKernelGGL(perm_scan, dim3(1), dim3(1024), 0, s, counts, nb, E, offsets, ext_T, t);
   hipLaunchKernelGGL(perm_scatter, dim3(nb), dim3(64), 0, s, ids, n, k, E, counts, src, inv);
   const hipError_t e = hipGetLastError();
+  if (e == hipSuccess && tiles_done) *tiles_done = t.bm > 0;
   if (e != hipSuccess || ext_T <= 0) return e;
   return launch_extend_shared(offsets, E, n, ext_T, src, s);
 }

@@ -27,26 +27,20 @@ __device__ inline void write_tile_lists(int* scan, const int* first, int G, cons
     scan[e] += v;
     __syncthreads();
   }
-  // entry idx belongs to the group x with scan[x - 1] * nn <= idx < scan[x] * nn
-  // (found by bisection)
+  // one work item per (group, n-tile): its c_g m-tiles are entries
+  // (scan[g] - c_g) * nn + nt * c_g + i, i < c_g
   for (int list = 0; list < 2; ++list) {
     const int nn = list ? t.ntn2 : t.ntn;
     int4* out = list ? t.tiles2 : t.tiles;
     if (nn <= 0) break;
     const int total = scan[1023] * nn;
-    for (int idx = e; idx < total; idx += 1024) {
-      int lo = 0, hi = G - 1;  // smallest x with scan[x] * nn > idx
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (scan[mid] * nn > idx) hi = mid;
-        else lo = mid + 1;
-      }
-      const int x = lo;
+    for (int w = e; w < G * nn; w += 1024) {
+      const int x = w / nn, nt = w - x * nn;
       const int c = scan[x] - (x > 0 ? scan[x - 1] : 0);
-      const int local = idx - (scan[x] - c) * nn;
-      const int nt = local / c, i = local - nt * c;
       const int r0 = first[x], n = first[x + 1] - r0;
-      out[idx] = make_int4(x, r0 + (int)((int64_t)i * n / c), r0 + (int)((int64_t)(i + 1) * n / c), nt);
+      const int base = (scan[x] - c) * nn + nt * c;
+      for (int i = 0; i < c; ++i)
+        out[base + i] = make_int4(x, r0 + (int)((int64_t)i * n / c), r0 + (int)((int64_t)(i + 1) * n / c), nt);
     }
     if (e == 0) *(list ? t.n_tiles2 : t.n_tiles) = total;
   }
