@@ -39,9 +39,6 @@ template <> struct Mma<MOE_DT_F32> {
   }
 };
 
-__device__ __forceinline__ float silu_mul(float g, float u) {
-  return g / (1.0f + __expf(-g)) * u;
-}
 
 template <int DT, int WM, int WN, int TM, int TN, int EPI, int ODT>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {

@@ -27,8 +27,6 @@ __device__ __forceinline__ f32x16 mma_fp8(const u32x4& a0, const u32x4& a1, cons
 
 typedef __attribute__((address_space(4))) const float cfloat;
 
-__device__ __forceinline__ float silu_mul8(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
-
 template <int WM, int WN, int TM, int TN, int EPI>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_kernel(GemmFp8Params p) {
   constexpr int NT = WM * WN * 64;
@@ -216,7 +214,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_kernel(GemmFp8Params p)
           const int col = nt * (BN / 2) + (wn * (TN / 2) + j) * 32 + lr;
           if (col < p.N)
             ((uint16_t*)p.C)[(int64_t)prow * p.N + col] =
-                (uint16_t)f32_to_bf16_bits(silu_mul8(acc[i][j][e], acc[i][j + TN / 2][e]));
+                (uint16_t)f32_to_bf16_bits(silu_mul(acc[i][j][e], acc[i][j + TN / 2][e]));
         }
       } else if constexpr (EPI == EPI_SCATTER) {
         const int tok = p.c_rows ? p.c_rows[prow] : prow;
@@ -578,7 +576,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_fp8_split_kernel(GemmFp8
       for (int jo = 0; jo < JO; ++jo)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          hv[i][jo][e] = silu_mul8(acc[i][jo][e], acc[i][jo + TN / 2][e]);
+          hv[i][jo][e] = silu_mul(acc[i][jo][e], acc[i][jo + TN / 2][e]);
           m = fmaxf(m, fabsf(hv[i][jo][e]));
         }
       m = fmaxf(m, __shfl_xor(m, 32, 64));
@@ -668,7 +666,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_fp8_split_kernel(GemmFp8
           const int col = nt * (BN / 2) + (wn * (TN / 2) + j) * 32 + lr;
           if (col < p.N)
             ((uint16_t*)p.C)[(int64_t)prow * p.N + col] =
-                (uint16_t)f32_to_bf16_bits(silu_mul8(acc[i][j][e], acc[i][j + TN / 2][e]));
+                (uint16_t)f32_to_bf16_bits(silu_mul(acc[i][j][e], acc[i][j + TN / 2][e]));
         }
       } else if constexpr (EPI == EPI_SCATTER) {
         const int tok = p.c_rows ? p.c_rows[prow] : prow;

@@ -49,8 +49,6 @@ __device__ __forceinline__ void pipe_schedule() {
   pipe_schedule_mfmas<0, NSUB * NL * TN, LI>();
 }
 
-__device__ __forceinline__ float silu_mul_p(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
-
 template <int TM, int TN, int S, int OCC, int ROWB, int EPI, int ODT>
 __global__ __launch_bounds__(256, OCC) void gemm_pipe_kernel(GemmParams p) {
   constexpr int WM = 2, WN = 2, NW = 4, NT = 256;
@@ -226,7 +224,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_pipe_kernel(GemmParams p) {
           const int col = nt * (BN / 2) + (wn * (TN / 2) + j) * 32 + lr;
           if (col < p.N)
             Elem<ODT>::store((typename Elem<ODT>::T*)p.C, (int64_t)prow * p.N + col,
-                             silu_mul_p(acc[i][j][e], acc[i][j + TN / 2][e]));
+                             silu_mul(acc[i][j][e], acc[i][j + TN / 2][e]));
         }
       } else if constexpr (EPI == EPI_SCATTER) {
         const int tok = p.c_rows ? p.c_rows[prow] : prow;
@@ -466,8 +464,8 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_split_kernel(GemmParams 
         for (int e = 0; e < 16; e += 2) {
           float v0, v1;
           if constexpr (EPI == EPI_SWIGLU) {
-            v0 = silu_mul_p(acc[i][jo][e], acc[i][jo + TN / 2][e]);
-            v1 = silu_mul_p(acc[i][jo][e + 1], acc[i][jo + TN / 2][e + 1]);
+            v0 = silu_mul(acc[i][jo][e], acc[i][jo + TN / 2][e]);
+            v1 = silu_mul(acc[i][jo][e + 1], acc[i][jo + TN / 2][e + 1]);
           } else {
             v0 = acc[i][jo][e];
             v1 = acc[i][jo][e + 1];
@@ -505,7 +503,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_split_kernel(GemmParams 
           const int col = nt * (BN / 2) + (wn * (TN / 2) + j) * 32 + lr;
           if (col < p.N)
             Elem<ODT>::store((typename Elem<ODT>::T*)p.C, (int64_t)prow * p.N + col,
-                             silu_mul_p(acc[i][j][e], acc[i][j + TN / 2][e]));
+                             silu_mul(acc[i][j][e], acc[i][j + TN / 2][e]));
         }
       } else if constexpr (EPI == EPI_SCATTER) {
         const int tok = p.c_rows ? p.c_rows[prow] : prow;

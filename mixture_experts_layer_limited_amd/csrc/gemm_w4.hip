@@ -49,8 +49,6 @@ namespace moe {
 
 namespace {
 
-__device__ __forceinline__ float silu_mul_w4(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
-
 // Eight 4-bit codes (code i in bits 4i..4i+3 of w) as bf16 values 136 + q_i,
 // pairs (0,4), (1,5), (2,6), (3,7).
 __device__ __forceinline__ u32x4 widen_w4(uint32_t w) {
@@ -371,7 +369,7 @@ __global__ __launch_bounds__(512, 1) void gemm_w4_kernel(GemmW4Params p) {
             const int col = ct.nt * (BN / 2) + (wn * (NB / 2) + jb) * 16 + n16;
             const uint32_t off = (row < rows && col < p.N) ? (uint32_t)((row * p.N + col) * 2) : 0x80000000u;
             __builtin_amdgcn_raw_buffer_store_b16(
-                (unsigned short)f32_to_bf16_bits(silu_mul_w4(acc[jb][r], acc[jb + NB / 2][r])), rc, off, 0, 0);
+                (unsigned short)f32_to_bf16_bits(silu_mul(acc[jb][r], acc[jb + NB / 2][r])), rc, off, 0, 0);
           }
         } else {
 #pragma unroll
