@@ -41,22 +41,47 @@ __global__ __launch_bounds__(256) void perm_hist(const int32_t* __restrict__ ids
 // counts[b][e] in place into the first permuted slot of chunk b for expert e.
 // With t.bm > 0 it also writes the GEMMs' tile lists over the E groups (E + 1
 // with the shared expert's ext_T rows as group E).
+// When the nb x E counts fit kScanStash entries, all 1024 threads first copy
+// them into LDS with coalesced loads, all issued before the first wait, and
+// both passes over them read LDS: the stores of the second pass then never
+// hold up a load (the vector memory counter retires in order).
+constexpr int kScanStash = 32768;  // 128 KB
+
 __global__ __launch_bounds__(1024) void perm_scan(int32_t* __restrict__ counts, int nb, int E,
                                                   int32_t* __restrict__ offsets, int ext_T, TileLists t) {
   __shared__ int scan[1024];
   __shared__ int first[1026];
+  __shared__ int stash[kScanStash];
   const int e = threadIdx.x;
-  int total = 0;
-  if (e < E) {  // 8 chunks' counts in flight at a time
-    int b = 0;
-    for (; b + 8 <= nb; b += 8) {
+  const bool staged = (int64_t)nb * E <= kScanStash;
+  const int nall = staged ? nb * E : 0;
+  if (staged) {
+    int i = e;
+    for (; i + 7 * 1024 < nall; i += 8 * 1024) {
       int c[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) c[u] = counts[(int64_t)(b + u) * E + e];
+      for (int u = 0; u < 8; ++u) c[u] = counts[i + u * 1024];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) total += c[u];
+      for (int u = 0; u < 8; ++u) stash[i + u * 1024] = c[u];
     }
-    for (; b < nb; ++b) total += counts[(int64_t)b * E + e];
+    for (; i < nall; i += 1024) stash[i] = counts[i];
+    __syncthreads();
+  }
+  int total = 0;
+  if (e < E) {
+    if (staged) {
+      for (int b = 0; b < nb; ++b) total += stash[b * E + e];
+    } else {  // 8 chunks' counts in flight at a time
+      int b = 0;
+      for (; b + 8 <= nb; b += 8) {
+        int c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c[u] = counts[(int64_t)(b + u) * E + e];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) total += c[u];
+      }
+      for (; b < nb; ++b) total += counts[(int64_t)b * E + e];
+    }
   }
   scan[e] = total;
   __syncthreads();
@@ -71,21 +96,29 @@ __global__ __launch_bounds__(1024) void perm_scan(int32_t* __restrict__ counts, 
     offsets[e] = excl;
     first[e] = excl;
     int run = excl;
-    int b = 0;
-    for (; b + 8 <= nb; b += 8) {
-      int c[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) c[u] = counts[(int64_t)(b + u) * E + e];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        counts[(int64_t)(b + u) * E + e] = run;
-        run += c[u];
+    if (staged) {
+      for (int b = 0; b < nb; ++b) {
+        const int c = stash[b * E + e];
+        counts[(int64_t)b * E + e] = run;
+        run += c;
       }
-    }
-    for (; b < nb; ++b) {
-      const int c = counts[(int64_t)b * E + e];
-      counts[(int64_t)b * E + e] = run;
-      run += c;
+    } else {
+      int b = 0;
+      for (; b + 8 <= nb; b += 8) {
+        int c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c[u] = counts[(int64_t)(b + u) * E + e];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          counts[(int64_t)(b + u) * E + e] = run;
+          run += c[u];
+        }
+      }
+      for (; b < nb; ++b) {
+        const int c = counts[(int64_t)b * E + e];
+        counts[(int64_t)b * E + e] = run;
+        run += c;
+      }
     }
   }
   if (e == E - 1) {
@@ -103,17 +136,27 @@ __global__ __launch_bounds__(64) void perm_scatter(const int32_t* __restrict__ i
                                                    const int32_t* __restrict__ first,
                                                    int32_t* __restrict__ src, int32_t* __restrict__ inv) {
   __shared__ int run[1024];
+  // the chunk's experts, loaded up front (the ranking loop's stores would
+  // otherwise hold up each of its loads: the vector memory counter retires in order)
+  __shared__ int eid[kChunk];
   const int lane = threadIdx.x;
+  const int base = blockIdx.x * kChunk;
+  {
+    int c[kChunk / 64];
+#pragma unroll
+    for (int u = 0; u < kChunk / 64; ++u) c[u] = ids[min(base + u * 64 + lane, n - 1)];  // n >= 1; copies past n unused
+#pragma unroll
+    for (int u = 0; u < kChunk / 64; ++u) eid[u * 64 + lane] = min(max(c[u], 0), E - 1);
+  }
   for (int e = lane; e < E; e += 64) run[e] = first[(int64_t)blockIdx.x * E + e];
   __syncthreads();
   int bits = 0;
   while ((1 << bits) < E) ++bits;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int base = blockIdx.x * kChunk;
   for (int g = 0; g < kChunk; g += 64) {
     const int a = base + g + lane;
     const bool ok = a < n;
-    const int e = ok ? min(max(ids[a], 0), E - 1) : 0;
+    const int e = ok ? eid[g + lane] : 0;
     uint64_t same = __ballot(ok);
     for (int b = 0; b < bits; ++b) {
       const bool bit = (e >> b) & 1;
@@ -147,10 +190,18 @@ __global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ i
   __shared__ int run[1024];  // counts, then the next free slot of each expert
   __shared__ int scan[1024];
   __shared__ int first[1026];  // the groups' first rows (tile lists)
+  // Each assignment's expert, kept from the histogram pass: the serial ranking
+  // below then issues no global loads, which would each wait (in-order vector
+  // memory counter) for every store issued before them.
+  __shared__ int eid[kSmallPermute];
   const int tid = threadIdx.x;
   run[tid] = 0;
   __syncthreads();
-  for (int a = tid; a < n; a += 1024) atomicAdd(&run[min(max(ids[a], 0), E - 1)], 1);
+  for (int a = tid; a < n; a += 1024) {
+    const int e = min(max(ids[a], 0), E - 1);
+    eid[a] = e;
+    atomicAdd(&run[e], 1);
+  }
   __syncthreads();
   const int cnt = tid < E ? run[tid] : 0;
   scan[tid] = cnt;
@@ -182,7 +233,7 @@ __global__ __launch_bounds__(1024) void perm_small(const int32_t* __restrict__ i
     for (int g = 0; g < n; g += 64) {
       const int a = g + lane;
       const bool ok = a < n;
-      const int e = ok ? min(max(ids[a], 0), E - 1) : 0;
+      const int e = ok ? eid[a] : 0;
       uint64_t same = __ballot(ok);
       for (int b = 0; b < bits; ++b) {
         const bool bit = (e >> b) & 1;

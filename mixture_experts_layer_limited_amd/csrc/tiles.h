@@ -34,13 +34,36 @@ __device__ inline void write_tile_lists(int* scan, const int* first, int G, cons
     int4* out = list ? t.tiles2 : t.tiles;
     if (nn <= 0) break;
     const int total = scan[1023] * nn;
-    for (int w = e; w < G * nn; w += 1024) {
-      const int x = w / nn, nt = w - x * nn;
+    // this thread's items w = x * nn + nt = e, e + 1024, ..., stepped without
+    // a division per item
+    const int dx = 1024 / nn, dnt = 1024 - dx * nn;
+    int x = e / nn, nt = e - x * nn;
+    while (x < G) {
       const int c = scan[x] - (x > 0 ? scan[x - 1] : 0);
       const int r0 = first[x], n = first[x + 1] - r0;
       const int base = (scan[x] - c) * nn + nt * c;
-      for (int i = 0; i < c; ++i)
-        out[base + i] = make_int4(x, r0 + (int)((int64_t)i * n / c), r0 + (int)((int64_t)(i + 1) * n / c), nt);
+      if (c > 0) {
+        // m-tile i: rows [r0 + floor(i n / c), r0 + floor((i + 1) n / c)), with
+        // floor(i n / c) = i q + floor(i r / c) for n = q c + r, stepped in i
+        const int q = n / c, r = n - q * c;
+        int lo = r0, acc = 0;
+        for (int i = 0; i < c; ++i) {
+          int hi = lo + q;
+          acc += r;
+          if (acc >= c) {
+            acc -= c;
+            ++hi;
+          }
+          out[base + i] = make_int4(x, lo, hi, nt);
+          lo = hi;
+        }
+      }
+      x += dx;
+      nt += dnt;
+      if (nt >= nn) {
+        nt -= nn;
+        ++x;
+      }
     }
     if (e == 0) *(list ? t.n_tiles2 : t.n_tiles) = total;
   }

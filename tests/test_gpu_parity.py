@@ -156,6 +156,8 @@ def test_permute_walkthrough_example():
     (16384, 256, 8, "random"), (777, 1024, 32, "random"), (3000, 64, 6, "one"), (128, 256, 8, "skew"),
     (129, 3, 2, "random"),
     (512, 64, 8, "random"), (513, 64, 8, "random"),   # 4096 copies (one work-group) and just past it
+    # chunk x expert counts: 16384 x 256 fills the scan's LDS copy exactly; 4500 x 1024 overflows it
+    (4500, 1024, 8, "random"),
 ])
 def test_permute_bit_exact(T, E, k, mode):
     say(f"permute T={T} E={E} k={k} {mode}")
