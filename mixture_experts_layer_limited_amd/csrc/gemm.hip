@@ -253,9 +253,11 @@ static hipError_t launch_cfg(const GemmParams& p, int grid_m, hipStream_t s) {
 
 // Tile shapes by kind.  Register-staged kernel (fp32, and bf16 buffers past 2 GiB):
 //   0: 2x2 waves of 2x2 32x32 blocks -> 128 x 128;  1: 1x4 waves of 1x2 -> 32 x 256.
-// Pipelined bf16 kernels (gemm_pipe.hip): 12: 128 x 256 single ring; 14: 64 x 256
-// single ring (decode-sized groups and the split-K router); 15: 256 x 256 split
-// rings (prefill-sized groups).  MOE_TILE_GEMM1 / MOE_TILE_GEMM2 force a kind for
+// Pipelined bf16 kernels (gemm_pipe.hip): 12: 128 x 256 single ring; 13: 64 x 256
+// single ring of 64-byte K rows, two work-groups per CU (the down GEMM of
+// decode-sized groups); 14: 64 x 256 single ring (the gate/up GEMM of
+// decode-sized groups and the split-K router); 15: 256 x 256 split rings
+// (prefill-sized groups).  MOE_TILE_GEMM1 / MOE_TILE_GEMM2 force a kind for
 // the gate/up or down GEMM at build time (tuning).
 #ifndef MOE_TILE_GEMM1
 #define MOE_TILE_GEMM1 -1
@@ -267,6 +269,7 @@ static int tile_bm(int kind) {
   switch (kind) {
     case 1: return 32;
     case 12: return 128;
+    case 13: return 64;
     case 14: return 64;
     case 15: return 256;
     default: return 128;
@@ -280,13 +283,13 @@ static int tile_bn(int kind) { return kind == 0 ? 128 : 256; }
 GemmShape gemm_shape(int which, int dt, int rows_hint, int64_t a_bytes, int64_t b_bytes) {
   int kind;
   if (which == 2) kind = dt == MOE_DT_BF16 ? 14 : 0;  // router: 64 x 256 tiles, split K
-  else if (rows_hint <= 32) kind = dt == MOE_DT_BF16 ? 14 : 1;
+  else if (rows_hint <= 32) kind = dt == MOE_DT_BF16 ? (which == 1 ? 13 : 14) : 1;
   else if (rows_hint < 128) kind = dt == MOE_DT_BF16 ? 12 : 0;
   else kind = dt == MOE_DT_BF16 ? 15 : 0;
   const bool pipe_ok = dt == MOE_DT_BF16 && a_bytes < (1LL << 31) && b_bytes < (1LL << 31);
   if (which == 0 && MOE_TILE_GEMM1 >= 0) kind = MOE_TILE_GEMM1;
   if (which == 1 && MOE_TILE_GEMM2 >= 0) kind = MOE_TILE_GEMM2;
-  if (kind != 0 && kind != 1 && kind != 12 && kind != 14 && kind != 15) kind = 0;
+  if (kind != 0 && kind != 1 && kind != 12 && kind != 13 && kind != 14 && kind != 15) kind = 0;
   if (kind >= 10 && !pipe_ok) kind = 0;
   GemmShape g;
   g.kind = kind;

@@ -558,12 +558,16 @@ static hipError_t launch_pipe(const GemmParams& p, int grid_m, hipStream_t s) {
 }
 
 // kind 12: 128 x 256, single ring of 3 slots of 128-byte K rows
+// kind 13:  64 x 256, single ring of 4 slots of 64-byte K rows, two work-groups
+//           per CU (decode down GEMM: its tiles are short, so one work-group's
+//           pipeline fill overlaps the other's stream)
 // kind 14:  64 x 256, single ring of 4 slots of 128-byte K rows (split K allowed)
 // kind 15: 256 x 256, split rings (A 2 slots + B 3 slots, 160 KB)
 template <int EPI, int ODT>
 static hipError_t pipe_kind(const GemmParams& p, const GemmShape& g, int grid_m, hipStream_t s) {
   switch (g.kind) {
     case 12: return launch_pipe<2, 4, 3, 1, 128, EPI, ODT>(p, grid_m, s);
+    case 13: return launch_pipe<1, 4, 4, 2, 64, EPI, ODT>(p, grid_m, s);
     case 14: return launch_pipe<1, 4, 4, 1, 128, EPI, ODT>(p, grid_m, s);
     case 15: return launch_split<2, 2, 4, 4, 2, 3, EPI, ODT>(p, grid_m, s);
     default: return hipErrorInvalidValue;
