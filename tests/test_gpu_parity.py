@@ -308,6 +308,61 @@ def test_forward_small(name, epi):
     assert err <= TOL[cfg.dtype]
 
 
+_BASE_PRESET = {"bf16": "v3_prefill_bf16", "fp8": "v3_fp8", "w4a16": "v3_decode_w4a16", "f32": "tiny_fp32"}
+
+
+def _random_layer(seed):
+    """A random valid layer: storage format, H, I, E, k, groups, shared width,
+    T from 1 to 1500, scoring, bias, renormalisation, scaling and epilogue;
+    T is halved until the fp64 oracle runs in about a second."""
+    rng = np.random.default_rng(seed)
+    dt = str(rng.choice(["bf16", "bf16", "fp8", "w4a16", "f32"]))
+    mult = 128 if dt in ("fp8", "w4a16") else 64
+    H = mult * int(rng.integers(1, 9))
+    I = mult * int(rng.integers(1, 7))
+    E = int(rng.choice([2, 3, 8, 16, 40, 64, 96, 160, 256, 300]))
+    ng = int(rng.choice([g for g in (1, 2, 4, 5, 8, 16) if E % g == 0 and (g == 1 or E // g >= 2)]))
+    tg = int(rng.integers(1, ng + 1))
+    kmax = E if ng == 1 else min(E, tg * (E // ng))
+    k = int(rng.integers(1, min(kmax, 32) + 1))
+    T = int(rng.choice([1, 2, 7, 33, 100, 257, 700, 1025, 1500]))
+    while T > 1 and T * k * H * I > 2e9:
+        T //= 2
+    scoring = "sigmoid" if (ng > 1 or rng.random() < 0.5) else "softmax"
+    cfg = PRESETS[_BASE_PRESET[dt]].replace(
+        name=f"random{seed}", tokens=T, hidden=H, inter=I, n_experts=E, top_k=k, n_group=ng, topk_group=tg,
+        shared_inter=int(rng.choice([0, I, 2 * I, mult])), scoring=scoring,
+        bias=str(rng.choice(["none", "zero"])) if scoring == "sigmoid" else "none",
+        norm_topk_prob=bool(rng.random() < 0.5), routed_scaling_factor=float(rng.choice([1.0, 2.5])))
+    return cfg, int(rng.integers(0, 2)), int(rng.integers(0, 1 << 30))
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_forward_random_layer(seed):
+    cfg, epi, input_seed = _random_layer(seed)
+    T, E, k, H = cfg.tokens, cfg.n_experts, cfg.top_k, cfg.hidden
+    say(f"forward random{seed}: {cfg.dtype} T={T} H={H} I={cfg.inter} E={E} k={k} groups={cfg.n_group}/"
+        f"{cfg.topk_group} Is={cfg.shared_inter} {cfg.scoring} bias={cfg.bias} epilogue={epi}")
+    inp = layer_inputs(cfg, input_seed, DEV)
+    c = binding_config(cfg)
+    out = torch.empty(T, H, dtype=inp["x"].dtype, device=DEV)
+    aux = moe.ForwardOutputs(scores=f32((T, E)), topk_ids=i32((T, k)), topk_w=f32((T, k)),
+                             expert_offsets=i32(E + 1), permuted_src=i32(T * k), inv_perm=i32(T * k))
+    moe.forward(c, T, inp["x"], inp["gate_w"], inp["bias"], inp["w13"], inp["w13_s"], inp["w2"], inp["w2_s"],
+                inp["sh_w13"], inp["sh_w13_s"], inp["sh_w2"], inp["sh_w2_s"], out, moe.workspace(c, T),
+                epilogue=epi, aux=aux)
+    torch.cuda.synchronize()
+    ids, w = oracle_routing(cfg, aux.scores.cpu().numpy(), inp["bias"])
+    assert np.array_equal(aux.topk_ids.cpu().numpy(), ids)
+    off, src, inv = oracle.permute(ids, E)
+    assert np.array_equal(aux.expert_offsets.cpu().numpy(), off)
+    assert np.array_equal(aux.permuted_src.cpu().numpy(), src)
+    assert np.array_equal(aux.inv_perm.cpu().numpy(), inv)
+    err = rel_err(f64(out), _oracle_full(cfg, inp, ids, w))
+    say(f"  max rel err {err:.3e} (tol {TOL[cfg.dtype]})")
+    assert err <= TOL[cfg.dtype]
+
+
 def test_forward_zero_tokens_is_a_no_op():
     cfg = SMALL["v3_small"]
     c = binding_config(cfg)
