@@ -186,8 +186,18 @@ __global__ __launch_bounds__(256) void gather_scales_t_kernel(const float* __res
                                                               float* __restrict__ scales_t) {
   const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (p >= rows) return;
-  const int64_t s = src ? src[p] : p;
-  for (int kb = 0; kb < nkb; ++kb) scales_t[(int64_t)kb * rows + p] = scales[s * nkb + kb];
+  const float* in = scales + (src ? (int64_t)src[p] : p) * nkb;
+  // 16 loads in flight before their stores (each load would otherwise wait
+  // for the stores before it: the vector memory counter retires in order)
+  int kb = 0;
+  for (; kb + 16 <= nkb; kb += 16) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = in[kb + u];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) scales_t[(int64_t)(kb + u) * rows + p] = v[u];
+  }
+  for (; kb < nkb; ++kb) scales_t[(int64_t)kb * rows + p] = in[kb];
 }
 
 hipError_t launch_gather_scales_t(const float* scales, const int32_t* src, int64_t rows, int nkb, float* scales_t,
