@@ -137,41 +137,47 @@ template <int IDT>
 __global__ __launch_bounds__(256) void quantize_kernel(int64_t rows, int64_t cols, const void* __restrict__ in,
                                                        uint8_t* __restrict__ codes, float* __restrict__ scales,
                                                        int64_t st_stride) {
-  // 16 lanes per 1x128 tile, 8 consecutive values per lane: one 16-byte (bf16)
-  // or two (fp32) loads and one 8-byte store of codes per lane.
+  // 8 lanes per 1x128 tile, 16 consecutive values per lane: two 16-byte (bf16)
+  // or four (fp32) loads, issued together, and two 8-byte stores of codes per lane.
   using T = typename Elem<IDT>::T;
-  const int lane = threadIdx.x & 63, sub = lane & 15;
+  const int lane = threadIdx.x & 63, sub = lane & 7;
   const int64_t tiles_per_row = cols / 128;
-  const int64_t tile = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int64_t tile = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
   if (tile >= rows * tiles_per_row) return;
   // row-major scales: consecutive tiles along a row; k-block-major scales:
   // consecutive tiles down a column of tiles, so the scale stores coalesce
   const int64_t r = st_stride > 0 ? tile % rows : tile / tiles_per_row;
   const int64_t c0 = (st_stride > 0 ? tile / rows : tile % tiles_per_row) * 128;
-  const int64_t base = r * cols + c0 + 8 * sub;
-  float v[8];
+  const int64_t base = r * cols + c0 + 16 * sub;
+  float v[16];
   if constexpr (IDT == MOE_DT_BF16) {
-    const u32x4 w = *(const u32x4*)((const T*)in + base);
+    const u32x4 w0 = *(const u32x4*)((const T*)in + base);
+    const u32x4 w1 = *(const u32x4*)((const T*)in + base + 8);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      v[2 * q] = __uint_as_float(w[q] << 16);
-      v[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+      v[2 * q] = __uint_as_float(w0[q] << 16);
+      v[2 * q + 1] = __uint_as_float(w0[q] & 0xffff0000u);
+      v[8 + 2 * q] = __uint_as_float(w1[q] << 16);
+      v[8 + 2 * q + 1] = __uint_as_float(w1[q] & 0xffff0000u);
     }
   } else {
-    const float4 w0 = *(const float4*)((const float*)in + base);
-    const float4 w1 = *(const float4*)((const float*)in + base + 4);
-    v[0] = w0.x; v[1] = w0.y; v[2] = w0.z; v[3] = w0.w;
-    v[4] = w1.x; v[5] = w1.y; v[6] = w1.z; v[7] = w1.w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 w = *(const float4*)((const float*)in + base + 4 * q);
+      v[4 * q] = w.x; v[4 * q + 1] = w.y; v[4 * q + 2] = w.z; v[4 * q + 3] = w.w;
+    }
   }
   float m = 0.0f;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(v[q]));
+  for (int q = 0; q < 16; ++q) m = fmaxf(m, fabsf(v[q]));
 #pragma unroll
-  for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  for (int o = 1; o < 8; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
   const float scale = m > 0.0f ? m / 448.0f : 1.0f;
-  const uint32_t lo = e4m3x4(v[0] / scale, v[1] / scale, v[2] / scale, v[3] / scale);
-  const uint32_t hi = e4m3x4(v[4] / scale, v[5] / scale, v[6] / scale, v[7] / scale);
-  *(uint2*)(codes + base) = make_uint2(lo, hi);
+  // two 8-byte stores: the codes buffer is only required to be 8-byte aligned
+  *(uint2*)(codes + base) = make_uint2(e4m3x4(v[0] / scale, v[1] / scale, v[2] / scale, v[3] / scale),
+                                       e4m3x4(v[4] / scale, v[5] / scale, v[6] / scale, v[7] / scale));
+  *(uint2*)(codes + base + 8) = make_uint2(e4m3x4(v[8] / scale, v[9] / scale, v[10] / scale, v[11] / scale),
+                                           e4m3x4(v[12] / scale, v[13] / scale, v[14] / scale, v[15] / scale));
   if (sub == 0) {
     if (st_stride > 0) scales[(c0 / 128) * st_stride + r] = scale;  // k-block-major
     else scales[r * tiles_per_row + c0 / 128] = scale;
@@ -212,7 +218,7 @@ hipError_t launch_quantize(int in_dt, int64_t rows, int64_t cols, const void* in
                            hipStream_t s, int64_t scales_t_stride) {
   const int64_t tiles = rows * (cols / 128);
   if (tiles <= 0) return hipSuccess;
-  const int64_t grid = (tiles + 15) / 16;
+  const int64_t grid = (tiles + 31) / 32;
   if (in_dt == MOE_DT_BF16)
     hipLaunchKernelGGL(quantize_kernel<MOE_DT_BF16>, dim3((unsigned)grid), dim3(256), 0, s, rows, cols, in, codes,
                        scales, scales_t_stride);
