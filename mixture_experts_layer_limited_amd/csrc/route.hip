@@ -17,7 +17,9 @@ namespace moe {
 // W tokens (waves) per work-group: 1 for small batches, so that the loads
 // of a split-K router's partial logits spread over as many CUs as there are
 // tokens; 4 for large ones.
-template <int V, int W>
+// NP: partial-logit slices whose loads are in flight at once (registers:
+// NP x V); a launch over few slices takes a small NP, so more waves fit a SIMD.
+template <int V, int W, int NP>
 __global__ __launch_bounds__(W * 64) void route_kernel(RouteParams p) {
   __shared__ float cs[W][V * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -35,9 +37,8 @@ __global__ __launch_bounds__(W * 64) void route_kernel(RouteParams p) {
     s[i] = valid[i] ? row[e] : 0.0f;
   }
   // logits of a split-K router GEMM: partial sums of K slices, added in slice
-  // order; the loads of up to NP slices are in flight at once (about 112
-  // registers), so a decode batch's 50-odd slices take two round trips
-  constexpr int NP = 112 / V < 32 ? (112 / V > 0 ? 112 / V : 1) : 32;
+  // order; the loads of up to NP slices are in flight at once, so a decode
+  // batch's 50-odd slices take two round trips
   for (int q0 = 1; q0 < p.n_parts; q0 += NP) {
     float part[NP][V];
 #pragma unroll
@@ -157,15 +158,23 @@ __global__ __launch_bounds__(W * 64) void route_kernel(RouteParams p) {
   }
 }
 
-template <int V>
-static hipError_t launch_v(const RouteParams& p, hipStream_t s) {
+template <int V, int NP>
+static hipError_t launch_vp(const RouteParams& p, hipStream_t s) {
   if (p.T <= 2048) {
-    hipLaunchKernelGGL((route_kernel<V, 1>), dim3(p.T), dim3(64), 0, s, p);
+    hipLaunchKernelGGL((route_kernel<V, 1, NP>), dim3(p.T), dim3(64), 0, s, p);
   } else {
     const int grid = (p.T + 3) / 4;
-    hipLaunchKernelGGL((route_kernel<V, 4>), dim3(grid), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((route_kernel<V, 4, NP>), dim3(grid), dim3(256), 0, s, p);
   }
   return hipGetLastError();
+}
+
+template <int V>
+static hipError_t launch_v(const RouteParams& p, hipStream_t s) {
+  // up to 4 slices (prefill-sized batches): 4 loads of V each in flight;
+  // more (decode): about 112 registers of loads in flight
+  if (p.n_parts <= 4) return launch_vp<V, 3>(p, s);
+  return launch_vp<V, (112 / V < 32 ? (112 / V > 0 ? 112 / V : 1) : 32)>(p, s);
 }
 
 hipError_t launch_route(const RouteParams& p, hipStream_t s) {
