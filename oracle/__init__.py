@@ -28,7 +28,7 @@ from .moe import (  # noqa: F401
 )
 from .e4m3 import (  # noqa: F401
     E4M3_MAX, e4m3_decode, e4m3_encode, quantize_1x128, dequantize_1x128,
-    dequantize_blocks,
+    quantize_dequantize_1x128, dequantize_blocks,
 )
 from .int4 import (  # noqa: F401
     INT4_GROUP, int4_decode, unpack_int4, dequantize_int4_groups,

@@ -87,8 +87,16 @@ def dequantize_1x128(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
             * np.asarray(scales, np.float64)[..., None]).reshape(R, C)
 
 
+def quantize_dequantize_1x128(v: np.ndarray) -> np.ndarray:
+    """The value an FP8 GEMM operand carries: v quantised per 1x128 tile by
+    quantize_1x128 (after its fp32 cast) and decoded back, fp64.  This is the
+    step applied to x before both expert GEMM inputs and to h after SiLU*up."""
+    return dequantize_1x128(*quantize_1x128(np.asarray(v, np.float64)))
+
+
 def dequantize_blocks(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """(N,K) weight from E4M3 codes and one fp32 scale per 128x128 block, fp64."""
+    """(N,K) weight from E4M3 codes and one fp32 scale per 128x128 block, fp64:
+    w[n, k] = value(codes[n, k]) * scales[n // 128, k // 128], scales (N/128, K/128)."""
     N, K = codes.shape
     v = e4m3_decode(codes).reshape(N // 128, 128, K // 128, 128)
     return (v * np.asarray(scales, np.float64)[:, None, :, None]).reshape(N, K)

@@ -68,9 +68,7 @@ class ExpertSource:
 def fp8_quantizers(cfg: LayerConfig):
     if cfg.dtype != "fp8":
         return None, None
-    def q(v):
-        return oracle.dequantize_1x128(*oracle.quantize_1x128(np.asarray(v, np.float64)))
-    return q, q
+    return oracle.quantize_dequantize_1x128, oracle.quantize_dequantize_1x128
 
 
 def oracle_routing(cfg: LayerConfig, gpu_scores: np.ndarray, bias):
