@@ -10,8 +10,10 @@ grouped SwiGLU GEMMs, shared expert, combine) through the C ABI.
 Prints one JSON line.  `value` is layer tokens/s; `roofline` is for the
 dominant kernel, the routed experts' gate/up GEMM with its SiLU*up epilogue,
 timed live with HIP events the library records around it on the layer's
-stream; `grouped_gemm` covers both routed GEMMs (gate/up and down);
-`cpu_baseline` times the fp64 CPU oracle on a sample of the same workload.
+stream; `grouped_gemm` covers both routed GEMMs (gate/up and down); `decode` times
+the V3 decode-shaped layer (T = 128, Zipf-skewed routing) the same way, as
+weight streaming against the HBM peak; `cpu_baseline` times the fp64 CPU
+oracle on a sample of the same workload shaped like the real batch.
 """
 import argparse
 import ctypes
@@ -67,8 +69,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="v3_prefill_bf16")
     p.add_argument("--epilogue", choices=["store", "scatter"], default="store")
-    p.add_argument("--cpu-sample", type=int, default=None,
-                   help="tokens in the oracle's timed sample (0 = skip; default: about 10-30 s of host work)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="about this much timed host work for the oracle's sample (0 = skip)")
+    p.add_argument("--decode-steps", type=int, default=200,
+                   help="timed forwards of the V3 decode layer reported beside the default workload (0 = skip)")
     return p.parse_args()
 
 
@@ -98,60 +102,182 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
-def cpu_baseline(cfg, inp, n_tokens):
-    """The fp64 oracle, as it stands, on the first n_tokens tokens of the batch:
-    fp64 router GEMM + scoring + group-limited top-k for those tokens, then
-    their expert FFNs and the shared expert with weights decoded from the
-    stored bf16 / E4M3 / 4-bit values.  Weights of the experts the sample
-    needs are copied to host memory first (not timed)."""
+def _blas_info():
+    from threadpoolctl import threadpool_info
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    threads = max([i.get("num_threads", 1) for i in blas] or [1])
+    vendor = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version') or ''}".strip() for i in blas})) or "none"
+    return int(threads), vendor
+
+
+def cpu_baseline(cfg, inp, min_seconds=10.0, max_experts=96):
+    """The fp64 oracle, as it stands, on a bounded sample shaped like the real
+    batch.  Timed: routing and permutation of all T tokens (fp64 router GEMM,
+    scoring, group-limited top-k); then, expert by expert in id order, the
+    expert FFN over every row the expert received (its real row count) until
+    about min_seconds of work or max_experts experts; then the shared expert
+    on the same number of tokens as the sample's routed rows / k.  Decoding the
+    stored bf16 / E4M3 / 4-bit weights to fp64 is not timed.  The layer time
+    is extrapolated per routed row (T*k rows) and per shared-expert token (T);
+    the combine (k*H multiply-adds per token, well under 1 % of the flops) is
+    left out."""
     import numpy as np
     import oracle
-    from threadpoolctl import threadpool_info
 
-    x = inp["x"][:n_tokens].float().cpu().double().numpy()
-    gw = inp["gate_w"].float().cpu().double().numpy()
-    bias = None if inp["bias"] is None else inp["bias"].cpu().double().numpy()
-    s, ids, w = oracle.route(x, gw, bias, scoring=cfg.scoring, top_k=cfg.top_k, n_group=cfg.n_group,
-                             topk_group=cfg.topk_group, norm_topk_prob=cfg.norm_topk_prob,
-                             routed_scaling_factor=cfg.routed_scaling_factor)
-    need = sorted({int(e) for e in ids.reshape(-1)})
+    T, H, I, Is, E, k = cfg.tokens, cfg.hidden, cfg.inter, cfg.shared_inter, cfg.n_experts, cfg.top_k
     fp8 = cfg.dtype == "fp8"
     scaled = cfg.dtype in ("fp8", "w4a16")
-    host = {e: tuple(inp[n][e].cpu() for n in (("w13", "w13_s", "w2", "w2_s") if scaled else ("w13", "w2")))
-            for e in need}
-    sh = tuple(inp[n].cpu() for n in (("sh_w13", "sh_w13_s", "sh_w2", "sh_w2_s") if scaled else ("sh_w13", "sh_w2")))
+    x = inp["x"].float().cpu().double().numpy()
+    gw = inp["gate_w"].float().cpu().double().numpy()
+    bias = None if inp["bias"] is None else inp["bias"].cpu().double().numpy()
 
-    def dec(t, sc=None):
-        if sc is None:
-            return t.float().double().numpy()
+    def dec(name, e=None):
+        t = inp[name] if e is None else inp[name][e]
+        if not scaled:
+            return t.float().cpu().double().numpy()
+        sc = (inp[name + "_s"] if e is None else inp[name + "_s"][e]).cpu().numpy()
         if fp8:
-            return oracle.dequantize_blocks(t.numpy(), sc.numpy())
-        return oracle.dequantize_int4_groups(t.numpy(), sc.numpy())
+            return oracle.dequantize_blocks(t.cpu().numpy(), sc)
+        return oracle.dequantize_int4_groups(t.cpu().numpy(), sc)
 
-    def get_expert(e):
-        h = host[e]
-        return (dec(h[0], h[1]), dec(h[2], h[3])) if scaled else (dec(h[0]), dec(h[1]))
-
-    def get_shared():
-        return (dec(sh[0], sh[1]), dec(sh[2], sh[3])) if scaled else (dec(sh[0]), dec(sh[1]))
-
-    q = None
-    if fp8:
-        def q(v):
-            return oracle.dequantize_1x128(*oracle.quantize_1x128(v))
+    q = oracle.quantize_dequantize_1x128 if fp8 else None
     t0 = time.perf_counter()
-    s, ids, w = oracle.route(x, gw, bias, scoring=cfg.scoring, top_k=cfg.top_k, n_group=cfg.n_group,
+    s, ids, w = oracle.route(x, gw, bias, scoring=cfg.scoring, top_k=k, n_group=cfg.n_group,
                              topk_group=cfg.topk_group, norm_topk_prob=cfg.norm_topk_prob,
                              routed_scaling_factor=cfg.routed_scaling_factor)
-    oracle.permute(ids, cfg.n_experts)
-    oracle.moe_layer_rows(np.arange(n_tokens), x, ids, w, get_expert, get_shared, quantize_x=q, quantize_h=q)
-    dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "seconds": dt,
-            "sample": f"first {n_tokens} tokens of the {cfg.tokens}-token batch: fp64 routing of those tokens, "
-                      f"their {len(need)} routed expert FFNs and the shared expert, weights decoded to fp64 "
-                      f"from the stored values"}
+    off, src, inv = oracle.permute(ids, E)
+    t_route = time.perf_counter() - t0
+    t_exp, rows, n_exp, flops = 0.0, 0, 0, 0.0
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        w13, w2 = dec("w13", e), dec("w2", e)
+        xs = x[src[lo:hi]]
+        t1 = time.perf_counter()
+        oracle.expert_outputs(xs, np.array([0, hi - lo]), np.arange(hi - lo), lambda g: (w13, w2), q, q)
+        t_exp += time.perf_counter() - t1
+        rows += hi - lo
+        n_exp += 1
+        flops += 6.0 * (hi - lo) * H * I
+        if t_route + t_exp >= 0.8 * min_seconds or n_exp >= max_experts:
+            break
+    n_sh, t_sh = 0, 0.0
+    if Is > 0:
+        n_sh = min(T, max(1, rows // k))
+        sh13, sh2 = dec("sh_w13"), dec("sh_w2")
+        t1 = time.perf_counter()
+        oracle.swiglu_ffn(x[:n_sh] if q is None else q(x[:n_sh]), sh13, sh2, q)
+        t_sh = time.perf_counter() - t1
+        flops += 6.0 * n_sh * H * Is
+    est = t_route + t_exp * (T * k / rows) + (t_sh * T / n_sh if n_sh else 0.0)
+    threads, vendor = _blas_info()
+    whole = rows == T * k
+    return {"value": T / est, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "seconds": t_route + t_exp + t_sh, "gflops_fp64": flops / (t_exp + t_sh) / 1e9, "blas": vendor,
+            "extrapolated": not whole,
+            "sample": (f"fp64 routing + permutation of all {T} tokens; routed expert FFNs of experts in id order "
+                       f"over every row each received: {n_exp} experts, {rows} of {T * k} rows (real per-expert "
+                       f"counts); shared expert on {n_sh} tokens; weights decoded to fp64 untimed"
+                       + ("" if whole else "; layer time extrapolated per routed row and per shared token"))}
+
+
+def time_layer(moe, torch, np, cfg, inp, epilogue, steps, warmup):
+    """Warm-up, then `steps` timed forwards of the layer: the region's mean per
+    forward, every forward's own time, and the routed gate/up and down GEMMs'
+    times from the events the library records on its stream."""
+    dev = "cuda"
+    c = moe.make_config(hidden=cfg.hidden, inter=cfg.inter, n_experts=cfg.n_experts, top_k=cfg.top_k,
+                        n_group=cfg.n_group, topk_group=cfg.topk_group, shared_inter=cfg.shared_inter,
+                        scoring=cfg.scoring, norm_topk_prob=cfg.norm_topk_prob,
+                        routed_scaling_factor=cfg.routed_scaling_factor, dtype=cfg.dtype)
+    T, E, H = cfg.tokens, cfg.n_experts, cfg.hidden
+    epi = moe.MOE_EPI_SCATTER_ADD if epilogue == "scatter" else moe.MOE_EPI_STORE_ROWS
+    out = torch.empty(T, H, dtype=inp["x"].dtype, device=dev)
+    ws = moe.workspace(c, T, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+
+    def step(events=None):
+        moe.forward(c, T, inp["x"], inp["gate_w"], inp["bias"], inp["w13"], inp["w13_s"], inp["w2"], inp["w2_s"],
+                    inp["sh_w13"], inp["sh_w13_s"], inp["sh_w2"], inp["sh_w2_s"], out, ws, epilogue=epi,
+                    aux=moe.ForwardOutputs(expert_offsets=offsets, events=events))
+
+    step()
+    torch.cuda.synchronize()
+    counts = np.diff(offsets.cpu().numpy())
+    non_empty = int((counts > 0).sum())
+    for _ in range(warmup):
+        step()
+    ev = HipEvents(4 * steps)
+    torch.cuda.synchronize()
+    # one event between consecutive steps: the whole region and every step's own time
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    marks[0].record()
+    for i in range(steps):
+        step(tuple(ev.ev[4 * i:4 * i + 4]))
+        marks[i + 1].record()
+    torch.cuda.synchronize()
+    ms = marks[0].elapsed_time(marks[-1]) / steps
+    per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(steps)])
+    g1 = float(np.mean([ev.ms(ev.ev[4 * i], ev.ev[4 * i + 1]) for i in range(steps)]))
+    g2 = float(np.mean([ev.ms(ev.ev[4 * i + 2], ev.ev[4 * i + 3]) for i in range(steps)]))
+    ev.close()
+    return ms, per_step, g1, g2, non_empty
+
+
+def work(cfg, epilogue, non_empty):
+    """Algorithmic flops and bytes of the routed gate/up GEMM (1), the routed
+    down GEMM (2) and the whole layer: each non-empty expert's weights once,
+    activations in, results out (padding rows, permuted copies and re-reads
+    are not counted)."""
+    T, E, k, H, I, Is = cfg.tokens, cfg.n_experts, cfg.top_k, cfg.hidden, cfg.inter, cfg.shared_inter
+    eb = {"f32": 4, "bf16": 2, "fp8": 1, "w4a16": 0.5}[cfg.dtype]   # bytes per expert weight
+    ab = 4 if cfg.dtype == "f32" else 2                              # bytes per activation (x, out)
+    qb = 1 if cfg.dtype == "fp8" else ab                             # bytes per GEMM operand (x, h)
+    # With the routed experts' width, stored rows and T <= 1024, the shared expert runs
+    # as one more group of the routed GEMM launches, so the timed grouped GEMMs include it.
+    merged = Is == I and Is > 0 and epilogue == "store" and E < 1024 and T <= 1024
+    groups = non_empty + (1 if merged else 0)
+    rows = T * k + (T if merged else 0)
+    flops1 = 2.0 * rows * (2 * I) * H
+    flops2 = 2.0 * rows * H * I
+    bytes1 = groups * 2 * I * H * eb + T * H * qb + rows * I * qb
+    bytes2 = groups * H * I * eb + rows * I * qb + rows * H * ab
+    if cfg.dtype == "fp8":   # 128x128 weight-block scales, 1x128 activation scales (x in, h out, h in)
+        bytes1 += groups * (2 * I // 128) * (H // 128) * 4 + T * (H // 128) * 4 + rows * (I // 128) * 4
+        bytes2 += groups * (H // 128) * (I // 128) * 4 + rows * (I // 128) * 4
+    if cfg.dtype == "w4a16":  # one fp32 scale per weight row and 128 columns
+        bytes1 += groups * (2 * I) * (H // 128) * 4
+        bytes2 += groups * H * (I // 128) * 4
+    # the whole layer: router weight, every non-empty expert and the shared expert once, x in, out
+    sh_bytes = 3 * H * Is * eb if Is > 0 else 0
+    layer_bytes = E * H * ab + non_empty * 3 * I * H * eb + sh_bytes + 2 * T * H * ab
+    return dict(merged=merged, rows=rows, flops1=flops1, flops2=flops2, bytes1=bytes1, bytes2=bytes2,
+                layer_bytes=layer_bytes)
+
+
+def decode_object(moe, torch, np, layer_inputs, PRESETS, steps, warmup):
+    """The decode-shaped layer (V3 dims, T = 128, Zipf-skewed routing) timed the
+    same way: weight streaming against the HBM peak."""
+    cfg = PRESETS["v3_decode_bf16"]
+    print(f"[bench] drawing inputs for {cfg.name}", file=sys.stderr, flush=True)
+    inp = layer_inputs(cfg, 0, "cuda")
+    ms, per_step, g1, g2, non_empty = time_layer(moe, torch, np, cfg, inp, "store", steps, warmup)
+    w = work(cfg, "store", non_empty)
+    gemm_bytes = w["bytes1"] + w["bytes2"]
+    del inp
+    torch.cuda.empty_cache()
+    return {"workload": f"{cfg.name}: T={cfg.tokens} H={cfg.hidden} E={cfg.n_experts} I={cfg.inter} "
+                        f"k={cfg.top_k} groups {cfg.n_group}/{cfg.topk_group} sigmoid + Zipf(1.1)-calibrated bias, "
+                        f"shared Is={cfg.shared_inter}, bf16",
+            "steps": steps, "warmup": warmup, "ms_per_step": ms, "tokens_per_s": cfg.tokens / (ms * 1e-3),
+            "step_ms_median": float(np.median(per_step)), "non_empty_experts": non_empty,
+            "layer_bytes": w["layer_bytes"], "layer_gb_s": w["layer_bytes"] / (ms * 1e-3) / 1e9,
+            "layer_hbm_frac": w["layer_bytes"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "ms_gate_up": g1, "ms_down": g2, "grouped_gemm_bytes": gemm_bytes,
+            "grouped_gemm_gb_s": gemm_bytes / ((g1 + g2) * 1e-3) / 1e9,
+            "grouped_gemm_hbm_frac": gemm_bytes / ((g1 + g2) * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "shared_expert_included": w["merged"]}
 
 
 def main():
@@ -168,63 +294,12 @@ def main():
     from moe_inputs import PRESETS, layer_inputs
 
     cfg = PRESETS[a.config]
-    dev = "cuda"
     print(f"[bench] drawing inputs for {cfg.name} on {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
-    inp = layer_inputs(cfg, 0, dev)
-    c = moe.make_config(hidden=cfg.hidden, inter=cfg.inter, n_experts=cfg.n_experts, top_k=cfg.top_k,
-                        n_group=cfg.n_group, topk_group=cfg.topk_group, shared_inter=cfg.shared_inter,
-                        scoring=cfg.scoring, norm_topk_prob=cfg.norm_topk_prob,
-                        routed_scaling_factor=cfg.routed_scaling_factor, dtype=cfg.dtype)
+    inp = layer_inputs(cfg, 0, "cuda")
     T, E, k, H, I, Is = cfg.tokens, cfg.n_experts, cfg.top_k, cfg.hidden, cfg.inter, cfg.shared_inter
-    epi = moe.MOE_EPI_SCATTER_ADD if a.epilogue == "scatter" else moe.MOE_EPI_STORE_ROWS
-    out = torch.empty(T, H, dtype=inp["x"].dtype, device=dev)
-    ws = moe.workspace(c, T, device=dev)
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
-
-    def step(events=None):
-        moe.forward(c, T, inp["x"], inp["gate_w"], inp["bias"], inp["w13"], inp["w13_s"], inp["w2"], inp["w2_s"],
-                    inp["sh_w13"], inp["sh_w13_s"], inp["sh_w2"], inp["sh_w2_s"], out, ws, epilogue=epi,
-                    aux=moe.ForwardOutputs(expert_offsets=offsets, events=events))
-
-    step()
-    torch.cuda.synchronize()
-    counts = np.diff(offsets.cpu().numpy())
-    non_empty = int((counts > 0).sum())
-    for _ in range(a.warmup):
-        step()
-    ev = HipEvents(4 * a.steps)
-    torch.cuda.synchronize()
-    # one event between consecutive steps: the whole region and every step's own time
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
-    marks[0].record()
-    for i in range(a.steps):
-        step(tuple(ev.ev[4 * i:4 * i + 4]))
-        marks[i + 1].record()
-    torch.cuda.synchronize()
-    ms = marks[0].elapsed_time(marks[-1]) / a.steps
-    per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(a.steps)])
-    g1 = float(np.mean([ev.ms(ev.ev[4 * i], ev.ev[4 * i + 1]) for i in range(a.steps)]))
-    g2 = float(np.mean([ev.ms(ev.ev[4 * i + 2], ev.ev[4 * i + 3]) for i in range(a.steps)]))
-    ev.close()
-
-    eb = {"f32": 4, "bf16": 2, "fp8": 1, "w4a16": 0.5}[cfg.dtype]   # bytes per expert weight
-    ab = 4 if cfg.dtype == "f32" else 2
-    # With the routed experts' width, stored rows and T <= 1024, the shared expert runs
-    # as one more group of the routed GEMM launches, so the timed grouped GEMMs include it.
-    merged = Is == I and Is > 0 and a.epilogue == "store" and E < 1024 and T <= 1024
-    groups = non_empty + (1 if merged else 0)
-    rows = T * k + (T if merged else 0)
-    flops1 = 2.0 * rows * (2 * I) * H
-    flops2 = 2.0 * rows * H * I
-    # algorithmic bytes: weights of the groups that received rows, activations in, results out
-    bytes1 = groups * 2 * I * H * eb + T * H * ab + rows * I * ab
-    bytes2 = groups * H * I * eb + rows * I * ab + rows * H * ab
-    if cfg.dtype == "fp8":
-        bytes1 += groups * (2 * I // 128) * (H // 128) * 4 + T * (H // 128) * 4
-        bytes2 += groups * (H // 128) * (I // 128) * 4
-    if cfg.dtype == "w4a16":  # one fp32 scale per weight row and 128 columns
-        bytes1 += groups * (2 * I) * (H // 128) * 4
-        bytes2 += groups * H * (I // 128) * 4
+    ms, per_step, g1, g2, non_empty = time_layer(moe, torch, np, cfg, inp, a.epilogue, a.steps, a.warmup)
+    w = work(cfg, a.epilogue, non_empty)
+    flops1, flops2, bytes1, bytes2, merged = w["flops1"], w["flops2"], w["bytes1"], w["bytes2"], w["merged"]
     peak = PEAK_TFLOPS[cfg.dtype]
     ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
     intensity = flops1 / bytes1
@@ -238,7 +313,8 @@ def main():
     roof.update({"traffic": measured_traffic(cfg.name),
                  "kernel": "gate/up grouped GEMM with the SiLU*up epilogue (routed experts"
                            + (" + the shared expert as one more group)" if merged else ")"),
-                 "ms": g1, "algorithmic_bytes": bytes1, "algorithmic_flops": flops1})
+                 "ms": g1, "algorithmic_bytes": bytes1, "algorithmic_flops": flops1,
+                 "mfma_frac": flops1 / (g1 * 1e-3) / 1e12 / peak})
     gg_tflops = (flops1 + flops2) / ((g1 + g2) * 1e-3) / 1e12
     result = {
         "metric": METRIC,
@@ -253,13 +329,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.dtype == "w4a16" else cfg.dtype,
+        "dtype": cfg.dtype,
         "data": "synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights)",
         "config": {"workload": f"{cfg.name}: T={T} H={H} E={E} I={I} k={k} groups {cfg.n_group}/{cfg.topk_group} "
                                f"{cfg.scoring} shared Is={Is}", "tokens": T, "hidden": H, "experts": E,
                    "inter": I, "top_k": k, "shared_inter": Is, "epilogue": a.epilogue,
                    "expert_weights": {"f32": "fp32", "bf16": "bf16", "fp8": "E4M3 + 128x128 fp32 scales",
-                                      "w4a16": "int4 + fp32 scale per row and 128 columns"}[cfg.dtype],
+                                      "w4a16": "int4 + fp32 scale per row and 128 columns, bf16 MFMAs"}[cfg.dtype],
                    "non_empty_experts": non_empty},
         "grouped_gemm": {"ms_gate_up": g1, "ms_down": g2, "shared_expert_included": merged,
                          "tflops": gg_tflops, "peak_tflops": peak,
@@ -267,11 +343,13 @@ def main():
                          "gb_s": (bytes1 + bytes2) / ((g1 + g2) * 1e-3) / 1e9},
         "roofline": roof,
     }
-    # 4-bit weights are unpacked in numpy, which makes the oracle's per-token cost higher
-    sample = a.cpu_sample if a.cpu_sample is not None else (24 if cfg.dtype == "w4a16" else 40)
-    if sample > 0:
+    if a.cpu_seconds > 0:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(cfg, inp, sample)
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, min_seconds=a.cpu_seconds)
+    if a.config == "v3_prefill_bf16" and a.decode_steps > 0:
+        del inp
+        torch.cuda.empty_cache()
+        result["decode"] = decode_object(moe, torch, np, layer_inputs, PRESETS, a.decode_steps, a.warmup)
     print(json.dumps(result), flush=True)
 
 

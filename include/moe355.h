@@ -25,7 +25,10 @@
  *     down (H,Is) (walkthrough §2.2-§2.3 stacked storage, §3.3 x @ w.T);
  *   - index tensors are int32; T*k < 2^31; the hidden rows (T*H elements) and
  *     the intermediate rows ((T*k + T) * max(I, Is) elements) span less than
- *     2^31 bytes in the activation dtype (MOE_ERR_UNSUPPORTED otherwise);
+ *     2^31 bytes in the activation dtype, and so does every weight matrix (one
+ *     expert's w13 or w2, the shared expert's, gate.weight) in its storage
+ *     type (MOE_ERR_UNSUPPORTED otherwise): the GEMMs address each with 32-bit
+ *     buffer offsets;
  *   - activation, weight and output tensors (hidden, gate_w, w13, w2, sh_w13,
  *     sh_w2, expert_out, acc, shared_out, out, quantiser input) start on a
  *     16-byte boundary, E4M3 code outputs on an 8-byte boundary, every other
@@ -200,7 +203,8 @@ int moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_ids,
  * Grouped SwiGLU expert FFN over the permuted rows (walkthrough §3.3.1 and its
  * one-kernel grouped GEMM segmented by expert offsets): for every expert e and
  * row p in [expert_offsets[e], expert_offsets[e+1]):
- *   x_p = hidden[permuted_src[p]]   (permuted_src == NULL: x_p = hidden[p])
+ *   x_p = hidden[permuted_src[p]]   (permuted_src == NULL: x_p = hidden[p],
+ *                                    which needs expert_offsets[E] <= T)
  *   y_p = (SiLU(x_p w13[e][0:I]^T) * (x_p w13[e][I:2I]^T)) w2[e]^T
  * in fp32 accumulation, SiLU and product in fp32, the intermediate rounded to
  * the activation dtype (bf16, or E4M3 with 1x128 scales for FP8 weights;
@@ -209,7 +213,9 @@ int moe_permute(const moe_config* cfg, int64_t T, const int32_t* topk_ids,
  *   hidden         [T,H] act_dtype, or E4M3 codes when hidden_scales != NULL
  *   hidden_scales  [T,H/128] fp32 1x128 scales of E4M3 codes, or NULL
  *   permuted_src, expert_offsets   as produced by moe_permute; the number of
- *                  rows is expert_offsets[E] <= T*k
+ *                  rows is expert_offsets[E] <= T*k; a permuted_src entry
+ *                  outside [0,T) is a caller error: its row reads zeros (no
+ *                  access outside hidden or hidden_scales), it is not reported
  *   w13, w2        weight_dtype; w13_scales [E,2I/128,H/128] and
  *                  w2_scales [E,H/128,I/128] fp32 for FP8 weights;
  *                  4-bit weights: w13 [E,2I,H/2] and w2 [E,H,I/2] bytes with
@@ -247,8 +253,14 @@ int moe_combine(const moe_config* cfg, int64_t T, const void* expert_out, const 
                 void* out, hipStream_t stream);
 
 /*
- * The whole layer: moe_route, moe_permute, moe_grouped_swiglu for the routed
- * experts and for the shared expert, moe_combine, all on `stream`.
+ * The whole layer (walkthrough §3: routing §3.1, permutation §3.2, grouped
+ * expert GEMMs and the shared expert §3.3, combine §3.4, the shape timeline
+ * of §3.5; V3 lab page §4 route()): moe_route, moe_permute,
+ * moe_grouped_swiglu for the routed experts and for the shared expert,
+ * moe_combine, all on `stream`.  With FP8 weights x is quantised once
+ * (1x128) for the routed and the shared experts, the router reads the
+ * unquantised x (walkthrough §8: the gate is not quantised), and h is
+ * quantised after SiLU(gate) * up.
  *   hidden [T,H], gate_w [E,H] act_dtype; bias [E] fp32 or NULL;
  *   w13, w2 (+ scales) as in moe_grouped_swiglu; sh_w13 [2Is,H], sh_w2 [H,Is]
  *   (+ scales [2Is/128,H/128], [H/128,Is/128] for FP8; packed [2Is,H/2],

@@ -27,8 +27,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_CONFIG", -3: "MOE
           -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP"}
 
 EXPORTS = ("moe_workspace_size", "moe_validate_config", "moe_route", "moe_permute", "moe_grouped_swiglu",
-           "moe_combine", "moe_forward", "moe_load_balance", "moe_quantize_fp8_1x128", "moe_strerror",
-           "moe_version")
+           "moe_combine", "moe_forward", "moe_load_balance", "moe_quantize_fp8_1x128",
+           "moe_strerror", "moe_version")
 
 
 class MoeError(RuntimeError):
@@ -94,7 +94,8 @@ def lib() -> ctypes.CDLL:
         L.moe_strerror.restype = ctypes.c_char_p
         L.moe_version.argtypes = []
         for name in ("moe_validate_config", "moe_route", "moe_permute", "moe_grouped_swiglu", "moe_combine",
-                     "moe_forward", "moe_load_balance", "moe_quantize_fp8_1x128", "moe_version"):
+                     "moe_forward", "moe_load_balance", "moe_quantize_fp8_1x128",
+                     "moe_version"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib

@@ -62,6 +62,14 @@ int check_cfg(const moe_config* c) {
   if (c->weight_dtype != c->act_dtype && !(has_scales(c) && c->act_dtype == MOE_BF16)) return MOE_ERR_UNSUPPORTED;
   const int mult = has_scales(c) ? 128 : 64;
   if (c->hidden % mult || c->inter % mult || c->shared_inter % mult) return MOE_ERR_UNSUPPORTED;
+  // The GEMMs address one weight matrix (an expert's w13 or w2, the shared
+  // expert's, the router's) with 32-bit buffer offsets: each spans < 2^31 bytes.
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t wide = c->shared_inter > c->inter ? c->shared_inter : c->inter;
+  const int64_t w13_elems = 2 * wide * (int64_t)c->hidden;
+  const int64_t w13_bytes = is_w4(c) ? w13_elems / 2 : w13_elems * (is_fp8(c) ? 1 : (int64_t)act_bytes(c));
+  if (w13_bytes >= lim) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)c->n_experts * c->hidden * (int64_t)act_bytes(c) >= lim) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -112,8 +120,7 @@ int max_mtiles(int64_t rows, int bm, int groups) {
 // K slices of the router GEMM: enough work-groups for the whole chip when T is
 // small (a divisor of H/64, at most 64).
 GemmShape router_shape(const moe_config* c, int64_t T) {
-  const int64_t eb = act_bytes(c);
-  return gemm_shape(2, act_dt(c), (int)T, T * c->hidden * eb, (int64_t)c->n_experts * c->hidden * eb);
+  return gemm_shape(2, act_dt(c), (int)T);
 }
 
 int router_splits(const moe_config* c, int64_t T) {
@@ -141,31 +148,22 @@ void carve_permute(Carver& cv, const moe_config* c, int64_t T, PermuteWs& w) {
 }
 
 // Tile shapes of the gate/up and down GEMMs of one grouped SwiGLU.
-GemmShape shape1(const moe_config* c, int64_t T, int64_t rows, int groups, int I) {
-  const int64_t eb = act_bytes(c);
-  return gemm_shape(0, act_dt(c), (int)(rows / groups), T * c->hidden * eb, (int64_t)2 * I * c->hidden * eb);
+GemmShape shape1(const moe_config* c, int64_t rows, int groups) {
+  return gemm_shape(0, act_dt(c), (int)(rows / groups));
 }
-GemmShape shape2(const moe_config* c, int64_t rows, int groups, int I) {
-  const int64_t eb = act_bytes(c);
-  return gemm_shape(1, act_dt(c), (int)(rows / groups), rows * I * eb, (int64_t)c->hidden * I * eb);
+GemmShape shape2(const moe_config* c, int64_t rows, int groups) {
+  return gemm_shape(1, act_dt(c), (int)(rows / groups));
 }
 
-GemmShape fp8_shape1(const moe_config* c, int64_t T, int64_t rows, int groups, int I) {
-  return gemm_fp8_shape((int)(rows / groups), T * c->hidden, (int64_t)2 * I * c->hidden);
-}
-GemmShape fp8_shape2(const moe_config* c, int64_t rows, int groups, int I) {
-  return gemm_fp8_shape((int)(rows / groups), rows * I, (int64_t)c->hidden * I);
-}
-
-GemmShape tile_shape1(const moe_config* c, int64_t T, int64_t rows, int groups, int I) {
-  if (is_fp8(c)) return fp8_shape1(c, T, rows, groups, I);
+GemmShape tile_shape1(const moe_config* c, int64_t rows, int groups) {
+  if (is_fp8(c)) return gemm_fp8_shape();
   if (is_w4(c)) return gemm_w4_shape();
-  return shape1(c, T, rows, groups, I);
+  return shape1(c, rows, groups);
 }
-GemmShape tile_shape2(const moe_config* c, int64_t rows, int groups, int I) {
-  if (is_fp8(c)) return fp8_shape2(c, rows, groups, I);
+GemmShape tile_shape2(const moe_config* c, int64_t rows, int groups) {
+  if (is_fp8(c)) return gemm_fp8_shape();
   if (is_w4(c)) return gemm_w4_shape();
-  return shape2(c, rows, groups, I);
+  return shape2(c, rows, groups);
 }
 
 // Workspace of one grouped SwiGLU over `rows` permuted rows of `groups` experts
@@ -173,26 +171,24 @@ GemmShape tile_shape2(const moe_config* c, int64_t rows, int groups, int I) {
 struct SwigluWs {
   int4* tiles1; int* ntiles1;
   int4* tiles2; int* ntiles2;
-  void* h;                    // intermediate, act dtype (bf16 for FP8 weights)
-  uint8_t* hq; float* h_scales; // FP8: E4M3 intermediate + 1x128 scales
+  void* h;                    // intermediate, act dtype (bf16 and fp32 weights, 4-bit weights: bf16)
+  uint8_t* hq; float* h_scales; // FP8: E4M3 intermediate + 1x128 scales, k-block-major
   uint8_t* xq; float* xs;
   float* xs_t;                // FP8: activation scales of the permuted rows, k-block-major
   float* row_w;
 };
 void carve_swiglu(Carver& cv, const moe_config* c, int64_t T, int64_t rows, int groups, int I,
                   bool quantize_x, bool scatter, SwigluWs& w) {
-  const int64_t avg = rows / groups;
-  (void)avg;
-  const GemmShape g1 = tile_shape1(c, T, rows, groups, I);
-  const GemmShape g2 = tile_shape2(c, rows, groups, I);
+  const GemmShape g1 = tile_shape1(c, rows, groups);
+  const GemmShape g2 = tile_shape2(c, rows, groups);
   // tile lists: every (m-tile, n-tile) pair of the gate/up and of the down GEMM
   w.tiles1 = cv.take<int4>((size_t)max_mtiles(rows, g1.bm, groups) * ntiles_n(I, g1.bn / 2) + 1);
   w.ntiles1 = cv.take<int>(1);
   w.tiles2 = cv.take<int4>((size_t)max_mtiles(rows, g2.bm, groups) * ntiles_n(c->hidden, g2.bn) + 1);
   w.ntiles2 = cv.take<int>(1);
   if (is_fp8(c)) {
-    // the pipelined gate/up kernel writes h already quantised; the register-staged one writes bf16 h
-    w.h = g1.kind == 1 ? nullptr : cv.take<uint16_t>((size_t)rows * I);
+    // the gate/up kernel writes h already quantised
+    w.h = nullptr;
     w.hq = cv.take<uint8_t>((size_t)rows * I);
     w.h_scales = cv.take<float>((size_t)rows * (I / 128));
     if (quantize_x) {
@@ -201,7 +197,7 @@ void carve_swiglu(Carver& cv, const moe_config* c, int64_t T, int64_t rows, int 
     } else {
       w.xq = nullptr; w.xs = nullptr;
     }
-    w.xs_t = g1.kind == 1 ? cv.take<float>((size_t)rows * (c->hidden / 128)) : nullptr;
+    w.xs_t = cv.take<float>((size_t)rows * (c->hidden / 128));
   } else {
     w.h = cv.take<char>((size_t)rows * I * act_bytes(c));
     w.hq = nullptr; w.h_scales = nullptr; w.xq = nullptr; w.xs = nullptr; w.xs_t = nullptr;
@@ -335,7 +331,6 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
     return MOE_OK;
   };
   const int H = c->hidden;
-  const int64_t avg = rows / groups;
   if (is_fp8(c)) {
     const uint8_t* xq = (const uint8_t*)hidden;
     const float* xs = hidden_scales;
@@ -343,8 +338,7 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
       HIP_TRY(launch_quantize(act_dt(c), T, H, hidden, w.xq, w.xs, s));
       xq = w.xq; xs = w.xs;
     }
-    const GemmShape g1 = fp8_shape1(c, T, rows, groups, I);
-    const GemmShape g2 = fp8_shape2(c, rows, groups, I);
+    const GemmShape g1 = gemm_fp8_shape(), g2 = gemm_fp8_shape();
     const bool dense = offsets == nullptr;
     const int ntn1 = ntiles_n(I, g1.bn / 2), ntn2 = ntiles_n(H, g2.bn);
     if (!dense && !tiles_ready) {
@@ -352,21 +346,15 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
                                  w.ntiles2));
     }
     GemmFp8Params p{};
-    p.A = xq; p.a_scales = xs; p.a_rows = src;
-    if (g1.kind == 1) {  // the pipelined kernel reads the scales k-block-major over permuted rows
-      HIP_TRY(launch_gather_scales_t(xs, src, rows, H / 128, w.xs_t, s));
-      p.a_scales = w.xs_t; p.as_stride = rows;
-    }
+    // the kernel reads the activation scales k-block-major over the permuted rows
+    HIP_TRY(launch_gather_scales_t(xs, src, rows, H / 128, T, w.xs_t, s));
+    p.A = xq; p.a_scales = w.xs_t; p.as_stride = rows; p.a_rows = src;
     p.B = (const uint8_t*)w13; p.b_scales = w13_s;
     p.b_gstride = (int64_t)2 * I * H; p.bs_gstride = (int64_t)(2 * I / 128) * (H / 128);
     if (sg) { p.B2 = (const uint8_t*)sg->w13; p.b2_scales = sg->w13_s; p.b2_group = sg->group; }
     p.K = H; p.N = I;
-    const int64_t hst = g2.kind == 1 ? rows : 0;  // k-block-major h scales for the pipelined kernel
-    if (g1.kind == 1) {  // the pipelined kernel quantises h in its epilogue
-      p.Cq = w.hq; p.Cs = w.h_scales; p.cs_stride = hst;
-    } else {
-      p.C = w.h;
-    }
+    // the epilogue quantises h (E4M3 + k-block-major 1x128 scales)
+    p.Cq = w.hq; p.Cs = w.h_scales; p.cs_stride = rows;
     p.a_nrows = T;
     set_tiles(p, dense, rows, g1.bm, w.tiles1, w.ntiles1);
     p.ntn = ntn1;
@@ -374,9 +362,8 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
     MOE_TRY(mark(0));
     HIP_TRY(launch_gemm_fp8(EPI_SWIGLU, p, g1, gm1, s));
     MOE_TRY(mark(1));
-    if (g1.kind != 1) HIP_TRY(launch_quantize(MOE_DT_BF16, rows, I, w.h, w.hq, w.h_scales, s, hst));
     GemmFp8Params q{};
-    q.A = w.hq; q.a_scales = w.h_scales; q.a_rows = nullptr; q.as_stride = hst;
+    q.A = w.hq; q.a_scales = w.h_scales; q.a_rows = nullptr; q.as_stride = rows;
     q.B = (const uint8_t*)w2; q.b_scales = w2_s;
     q.b_gstride = (int64_t)H * I; q.bs_gstride = (int64_t)(H / 128) * (I / 128);
     if (sg) { q.B2 = (const uint8_t*)sg->w2; q.b2_scales = sg->w2_s; q.b2_group = sg->group; }
@@ -440,8 +427,8 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
     return mark(3);
   }
   const int dt = act_dt(c);
-  const GemmShape g1 = shape1(c, T, rows, groups, I);
-  const GemmShape g2 = shape2(c, rows, groups, I);
+  const GemmShape g1 = shape1(c, rows, groups);
+  const GemmShape g2 = shape2(c, rows, groups);
   const bool dense = offsets == nullptr;
   const int ntn1 = ntiles_n(I, g1.bn / 2), ntn2 = ntiles_n(H, g2.bn);
   if (!dense && !tiles_ready) {
@@ -656,8 +643,8 @@ int moe_forward(const moe_config* c, int64_t T, const void* hidden, const void* 
   // Small batches: the permutation's one work-group also writes both GEMMs' tile
   // lists (when their m-tiles have one height).
   const int groups = E + (merged ? 1 : 0);
-  const GemmShape g1 = tile_shape1(c, T, rows_all, groups, c->inter);
-  const GemmShape g2 = tile_shape2(c, rows_all, groups, c->inter);
+  const GemmShape g1 = tile_shape1(c, rows_all, groups);
+  const GemmShape g2 = tile_shape2(c, rows_all, groups);
   TileLists tl;
   if (g1.bm == g2.bm) {
     tl.bm = g1.bm;

@@ -131,12 +131,11 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Activation quantisation, one 1x128 tile per 16 lanes:
+// Activation quantisation, one 1x128 tile per 8 lanes:
 // scale = fp32(amax / 448) (1 if amax == 0), code = E4M3(fp32(v / scale)).
 template <int IDT>
 __global__ __launch_bounds__(256) void quantize_kernel(int64_t rows, int64_t cols, const void* __restrict__ in,
-                                                       uint8_t* __restrict__ codes, float* __restrict__ scales,
-                                                       int64_t st_stride) {
+                                                       uint8_t* __restrict__ codes, float* __restrict__ scales) {
   // 8 lanes per 1x128 tile, 16 consecutive values per lane: two 16-byte (bf16)
   // or four (fp32) loads, issued together, and two 8-byte stores of codes per lane.
   using T = typename Elem<IDT>::T;
@@ -144,10 +143,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(int64_t rows, int64_t col
   const int64_t tiles_per_row = cols / 128;
   const int64_t tile = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
   if (tile >= rows * tiles_per_row) return;
-  // row-major scales: consecutive tiles along a row; k-block-major scales:
-  // consecutive tiles down a column of tiles, so the scale stores coalesce
-  const int64_t r = st_stride > 0 ? tile % rows : tile / tiles_per_row;
-  const int64_t c0 = (st_stride > 0 ? tile / rows : tile % tiles_per_row) * 128;
+  const int64_t r = tile / tiles_per_row;
+  const int64_t c0 = (tile % tiles_per_row) * 128;
   const int64_t base = r * cols + c0 + 16 * sub;
   float v[16];
   if constexpr (IDT == MOE_DT_BF16) {
@@ -178,21 +175,24 @@ __global__ __launch_bounds__(256) void quantize_kernel(int64_t rows, int64_t col
                                        e4m3x4(v[4] / scale, v[5] / scale, v[6] / scale, v[7] / scale));
   *(uint2*)(codes + base + 8) = make_uint2(e4m3x4(v[8] / scale, v[9] / scale, v[10] / scale, v[11] / scale),
                                            e4m3x4(v[12] / scale, v[13] / scale, v[14] / scale, v[15] / scale));
-  if (sub == 0) {
-    if (st_stride > 0) scales[(c0 / 128) * st_stride + r] = scale;  // k-block-major
-    else scales[r * tiles_per_row + c0 / 128] = scale;
-  }
+  if (sub == 0) scales[r * tiles_per_row + c0 / 128] = scale;
 }
 
 // scales_t[kb * rows + p] = scales[src(p) * nkb + kb]: the activation scales of the
 // permuted rows, k-block-major, so a GEMM step reads the scales of a row tile as
-// one contiguous run.
+// one contiguous run.  src(p) outside [0, src_rows) (rows the expert offsets do
+// not cover, or a caller's out-of-range index) reads nothing and gets scale 1.
 __global__ __launch_bounds__(256) void gather_scales_t_kernel(const float* __restrict__ scales,
                                                               const int32_t* __restrict__ src, int64_t rows, int nkb,
-                                                              float* __restrict__ scales_t) {
+                                                              int64_t src_rows, float* __restrict__ scales_t) {
   const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (p >= rows) return;
-  const float* in = scales + (src ? (int64_t)src[p] : p) * nkb;
+  const int64_t sp = src ? (int64_t)src[p] : p;
+  if (sp < 0 || sp >= src_rows) {
+    for (int kb = 0; kb < nkb; ++kb) scales_t[(int64_t)kb * rows + p] = 1.0f;
+    return;
+  }
+  const float* in = scales + sp * nkb;
   // 16 loads in flight before their stores (each load would otherwise wait
   // for the stores before it: the vector memory counter retires in order)
   int kb = 0;
@@ -206,25 +206,25 @@ __global__ __launch_bounds__(256) void gather_scales_t_kernel(const float* __res
   for (; kb < nkb; ++kb) scales_t[(int64_t)kb * rows + p] = in[kb];
 }
 
-hipError_t launch_gather_scales_t(const float* scales, const int32_t* src, int64_t rows, int nkb, float* scales_t,
-                                  hipStream_t s) {
+hipError_t launch_gather_scales_t(const float* scales, const int32_t* src, int64_t rows, int nkb, int64_t src_rows,
+                                  float* scales_t, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(gather_scales_t_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, scales, src,
-                     rows, nkb, scales_t);
+                     rows, nkb, src_rows, scales_t);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize(int in_dt, int64_t rows, int64_t cols, const void* in, uint8_t* codes, float* scales,
-                           hipStream_t s, int64_t scales_t_stride) {
+                           hipStream_t s) {
   const int64_t tiles = rows * (cols / 128);
   if (tiles <= 0) return hipSuccess;
   const int64_t grid = (tiles + 31) / 32;
   if (in_dt == MOE_DT_BF16)
     hipLaunchKernelGGL(quantize_kernel<MOE_DT_BF16>, dim3((unsigned)grid), dim3(256), 0, s, rows, cols, in, codes,
-                       scales, scales_t_stride);
+                       scales);
   else
     hipLaunchKernelGGL(quantize_kernel<MOE_DT_F32>, dim3((unsigned)grid), dim3(256), 0, s, rows, cols, in, codes,
-                       scales, scales_t_stride);
+                       scales);
   return hipGetLastError();
 }
 

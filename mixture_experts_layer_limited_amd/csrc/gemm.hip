@@ -1,6 +1,7 @@
-// Grouped "NT" GEMMs on gfx950 MFMA for the MoE layer: router GEMM, routed
-// experts (gate/up GEMM with a fused SiLU*up epilogue, down GEMM with a
-// row-store or a weighted scatter-add epilogue) and the shared expert.
+// Grouped "NT" fp32 GEMMs on gfx950 MFMA for fp32 MoE layers: router GEMM,
+// routed experts (gate/up GEMM with a fused SiLU*up epilogue, down GEMM with a
+// row-store or a weighted scatter-add epilogue) and the shared expert; plus the
+// tile-list builder every grouped GEMM uses.
 //
 // C[p, n] = sum_k A[src(p), k] * B[g][n, k]   for rows p of m-tile (g, r0, r1)
 //
@@ -22,14 +23,9 @@ namespace moe {
 
 // MFMA over one 32-byte K slice per lane pair: lanes 0-31 hold one 16-byte
 // chunk, lanes 32-63 the next.  A and B fragments use the same lane -> K map,
-// so the K order inside the slice does not matter.
+// so the K order inside the slice does not matter.  (bf16 layers run the
+// pipelined kernels of gemm_pipe.hip; this kernel serves fp32 layers.)
 template <int DT> struct Mma;
-template <> struct Mma<MOE_DT_BF16> {
-  __device__ __forceinline__ static void run(f32x16& acc, const u32x4& a, const u32x4& b) {
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
-  }
-};
 template <> struct Mma<MOE_DT_F32> {
   __device__ __forceinline__ static void run(f32x16& acc, const u32x4& a, const u32x4& b) {
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
@@ -251,7 +247,7 @@ static hipError_t launch_cfg(const GemmParams& p, int grid_m, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Tile shapes by kind.  Register-staged kernel (fp32, and bf16 buffers past 2 GiB):
+// Tile shapes by kind.  Register-staged kernel (fp32):
 //   0: 2x2 waves of 2x2 32x32 blocks -> 128 x 128;  1: 1x4 waves of 1x2 -> 32 x 256.
 // Pipelined bf16 kernels (gemm_pipe.hip): 12: 128 x 256 single ring; 13: 64 x 256
 // single ring of 64-byte K rows, two work-groups per CU (the down GEMM of
@@ -278,19 +274,20 @@ static int tile_bm(int kind) {
 static int tile_bn(int kind) { return kind == 0 ? 128 : 256; }
 
 // which: 0 = gate/up GEMM, 1 = down GEMM, 2 = router GEMM.  rows_hint = mean
-// rows per group; a_bytes / b_bytes = sizes of the activation buffer and of one
-// group's weights (the pipelined kernel addresses both with 31-bit offsets).
-GemmShape gemm_shape(int which, int dt, int rows_hint, int64_t a_bytes, int64_t b_bytes) {
+// rows per group.  bf16 always takes a pipelined kernel (the ABI bounds the
+// activation buffers and every weight matrix below 2^31 bytes, the reach of its
+// 32-bit buffer offsets); fp32 takes the register-staged one.
+GemmShape gemm_shape(int which, int dt, int rows_hint) {
   int kind;
-  if (which == 2) kind = dt == MOE_DT_BF16 ? 14 : 0;  // router: 64 x 256 tiles, split K
-  else if (rows_hint <= 32) kind = dt == MOE_DT_BF16 ? (which == 1 ? 13 : 14) : 1;
-  else if (rows_hint < 128) kind = dt == MOE_DT_BF16 ? 12 : 0;
-  else kind = dt == MOE_DT_BF16 ? 15 : 0;
-  const bool pipe_ok = dt == MOE_DT_BF16 && a_bytes < (1LL << 31) && b_bytes < (1LL << 31);
-  if (which == 0 && MOE_TILE_GEMM1 >= 0) kind = MOE_TILE_GEMM1;
-  if (which == 1 && MOE_TILE_GEMM2 >= 0) kind = MOE_TILE_GEMM2;
-  if (kind != 0 && kind != 1 && kind != 12 && kind != 13 && kind != 14 && kind != 15) kind = 0;
-  if (kind >= 10 && !pipe_ok) kind = 0;
+  if (dt != MOE_DT_BF16) kind = (which != 2 && rows_hint <= 32) ? 1 : 0;
+  else if (which == 2) kind = 14;  // router: 64 x 256 tiles, split K
+  else if (rows_hint <= 32) kind = which == 1 ? 13 : 14;
+  else if (rows_hint < 128) kind = 12;
+  else kind = 15;
+  if (dt == MOE_DT_BF16) {
+    if (which == 0 && MOE_TILE_GEMM1 >= 12 && MOE_TILE_GEMM1 <= 15) kind = MOE_TILE_GEMM1;
+    if (which == 1 && MOE_TILE_GEMM2 >= 12 && MOE_TILE_GEMM2 <= 15) kind = MOE_TILE_GEMM2;
+  }
   GemmShape g;
   g.kind = kind;
   g.bm = tile_bm(kind);
@@ -298,36 +295,23 @@ GemmShape gemm_shape(int which, int dt, int rows_hint, int64_t a_bytes, int64_t 
   return g;
 }
 
-template <int DT, int EPI, int ODT>
+template <int EPI, int ODT>
 static hipError_t dispatch_shape(const GemmParams& p, const GemmShape& g, int grid_m, hipStream_t s) {
-  if (g.kind == 1) return launch_cfg<DT, 1, 4, 1, 2, EPI, ODT>(p, grid_m, s);
-  return launch_cfg<DT, 2, 2, 2, 2, EPI, ODT>(p, grid_m, s);
-}
-
-template <int DT, int EPI>
-static hipError_t dispatch_odt(const GemmParams& p, const GemmShape& g, int odt, int grid_m, hipStream_t s) {
-  if (odt == MOE_DT_F32) return dispatch_shape<DT, EPI, MOE_DT_F32>(p, g, grid_m, s);
-  return dispatch_shape<DT, EPI, MOE_DT_BF16>(p, g, grid_m, s);
+  if (g.kind == 1) return launch_cfg<MOE_DT_F32, 1, 4, 1, 2, EPI, ODT>(p, grid_m, s);
+  return launch_cfg<MOE_DT_F32, 2, 2, 2, 2, EPI, ODT>(p, grid_m, s);
 }
 
 hipError_t launch_gemm(int dt, int epi, int odt, const GemmParams& p, const GemmShape& g, int grid_m,
                        hipStream_t s) {
-  if (g.kind >= 10) {
-    if (dt != MOE_DT_BF16) return hipErrorInvalidValue;
+  if (dt == MOE_DT_BF16) {
+    if (g.kind < 12) return hipErrorInvalidValue;
     return launch_gemm_pipe(epi, odt, p, g, grid_m, s);
   }
-  if (dt == MOE_DT_BF16) {
-    switch (epi) {
-      case EPI_STORE: return dispatch_odt<MOE_DT_BF16, EPI_STORE>(p, g, odt, grid_m, s);
-      case EPI_SWIGLU: return dispatch_odt<MOE_DT_BF16, EPI_SWIGLU>(p, g, odt, grid_m, s);
-      case EPI_SCATTER: return dispatch_shape<MOE_DT_BF16, EPI_SCATTER, MOE_DT_F32>(p, g, grid_m, s);
-      default: return hipErrorInvalidValue;
-    }
-  }
+  if (g.kind > 1) return hipErrorInvalidValue;
   switch (epi) {
-    case EPI_STORE: return dispatch_odt<MOE_DT_F32, EPI_STORE>(p, g, odt, grid_m, s);
-    case EPI_SWIGLU: return dispatch_odt<MOE_DT_F32, EPI_SWIGLU>(p, g, odt, grid_m, s);
-    case EPI_SCATTER: return dispatch_shape<MOE_DT_F32, EPI_SCATTER, MOE_DT_F32>(p, g, grid_m, s);
+    case EPI_STORE: return dispatch_shape<EPI_STORE, MOE_DT_F32>(p, g, grid_m, s);
+    case EPI_SWIGLU: return dispatch_shape<EPI_SWIGLU, MOE_DT_F32>(p, g, grid_m, s);
+    case EPI_SCATTER: return dispatch_shape<EPI_SCATTER, MOE_DT_F32>(p, g, grid_m, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -27,214 +27,6 @@ __device__ __forceinline__ f32x16 mma_fp8(const u32x4& a0, const u32x4& a1, cons
 
 typedef __attribute__((address_space(4))) const float cfloat;
 
-template <int WM, int WN, int TM, int TN, int EPI>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_fp8_kernel(GemmFp8Params p) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int BM = WM * TM * 32;
-  constexpr int BN = WN * TN * 32;
-  constexpr int CA = BM * 8 / NT;
-  constexpr int CB = BN * 8 / NT;
-  static_assert(CA * NT == BM * 8 && CB * NT == BN * 8, "tile / thread mismatch");
-  static_assert(EPI != EPI_SWIGLU || TN % 2 == 0, "SwiGLU pairs gate and up tiles");
-  static_assert(BM <= NT, "one activation scale per thread");
-  constexpr int STAGE = (BM + BN) * 8;                 // u32x4 per operand stage
-  extern __shared__ u32x4 lds4[];
-  float* sa_lds = (float*)(lds4 + 2 * STAGE);           // [2][BM]
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-
-  // device list: every (m-tile, n-tile) pair; dense: n_mtiles x ntn tiles
-  const int total = p.tiles ? *p.n_mtiles_dev : p.n_mtiles * p.ntn;
-  const int P = blockIdx.x;
-  if (P >= total) return;
-  const int L = xcd_remap(P, total);
-  int grp, r0, r1, nt;
-  if (p.tiles) {
-    const int4 t = p.tiles[L];
-    grp = t.x; r0 = t.y; r1 = t.z; nt = t.w;
-  } else {
-    const int mt = L / p.ntn;
-    nt = L - mt * p.ntn;
-    grp = 0; r0 = mt * BM; r1 = min(p.M, r0 + BM);
-  }
-  const int rows = r1 - r0;
-  const int64_t K = p.K;
-  const int nkb = p.K / 128;
-  const bool g2_ = p.B2 && grp == p.b2_group;
-  const uint8_t* Bg = g2_ ? p.B2 : p.B + (int64_t)grp * p.b_gstride;
-  const float* SBg = g2_ ? p.b2_scales : p.b_scales + (int64_t)grp * p.bs_gstride;
-
-  const uint8_t* aptr[CA];
-  bool aok[CA];
-  int aoff[CA];
-#pragma unroll
-  for (int i = 0; i < CA; ++i) {
-    const int q = tid + i * NT, r = q >> 3, c = q & 7;
-    aok[i] = r < rows;
-    int src = 0;
-    if (aok[i]) src = p.a_rows ? p.a_rows[r0 + r] : r0 + r;
-    aptr[i] = p.A + (int64_t)src * K + c * 16;
-    aoff[i] = r * 8 + (c ^ (r & 7));
-  }
-  // activation-scale row of thread tid (tid < BM)
-  const bool sok = tid < rows;
-  const float* sap = p.a_scales;
-  if (sok) sap += (int64_t)(p.a_rows ? p.a_rows[r0 + tid] : r0 + tid) * nkb;
-
-  const uint8_t* bptr[CB];
-  int boff[CB];
-#pragma unroll
-  for (int i = 0; i < CB; ++i) {
-    const int q = tid + i * NT, r = q >> 3, c = q & 7;
-    int wrow;
-    if constexpr (EPI == EPI_SWIGLU) {
-      int j = min(nt * (BN / 2) + (r % (BN / 2)), p.N - 1);
-      wrow = (r < BN / 2) ? j : p.N + j;
-    } else {
-      wrow = min(nt * BN + r, p.N - 1);
-    }
-    bptr[i] = Bg + (int64_t)wrow * K + c * 16;
-    boff[i] = (BM + r) * 8 + (c ^ (r & 7));
-  }
-
-  auto bblock = [&](int tn) {
-    if constexpr (EPI == EPI_SWIGLU)
-      return tn < TN / 2 ? wn * (TN / 2) + tn : WN * (TN / 2) + wn * (TN / 2) + (tn - TN / 2);
-    else
-      return wn * TN + tn;
-  };
-  // weight-block row (of 128) of every wave tile column
-  int sbrow[TN];
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int bb = bblock(j) * 32;
-    int wrow;
-    if constexpr (EPI == EPI_SWIGLU) {
-      const int j0 = min(nt * (BN / 2) + (bb % (BN / 2)), p.N - 1);
-      wrow = (bb < BN / 2) ? j0 : p.N + j0;
-    } else {
-      wrow = min(nt * BN + bb, p.N - 1);
-    }
-    sbrow[j] = wrow / 128;
-  }
-
-  f32x16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  int tm_live = 0;
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-    if ((wm * TM + i) * 32 < rows) tm_live = i + 1;
-
-  u32x4 ra[CA], rb[CB];
-  float rsa = 0.0f;
-#define MOE_GLOAD(kt_)                                                       \
-  do {                                                                       \
-    const int64_t ko_ = (int64_t)(kt_) * 128;                                \
-    _Pragma("unroll") for (int i = 0; i < CA; ++i) if (aok[i]) ra[i] =       \
-        *(const u32x4*)(aptr[i] + ko_);                                      \
-    _Pragma("unroll") for (int i = 0; i < CB; ++i) rb[i] =                   \
-        *(const u32x4*)(bptr[i] + ko_);                                      \
-    if (sok) rsa = sap[kt_];                                                 \
-  } while (0)
-#define MOE_SSTORE(buf_)                                                     \
-  do {                                                                       \
-    u32x4* s_ = lds4 + (buf_) * STAGE;                                        \
-    _Pragma("unroll") for (int i = 0; i < CA; ++i) if (aok[i]) s_[aoff[i]] = ra[i]; \
-    _Pragma("unroll") for (int i = 0; i < CB; ++i) s_[boff[i]] = rb[i];      \
-    if (tid < BM) sa_lds[(buf_) * BM + tid] = sok ? rsa : 0.0f;              \
-  } while (0)
-
-  MOE_GLOAD(0);
-  MOE_SSTORE(0);
-  __syncthreads();
-
-  const int sw = lane & 7, lr = lane & 31, hi = lane >> 5;
-  for (int kt = 0; kt < nkb; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nkb) MOE_GLOAD(kt + 1);
-    if (tm_live > 0) {
-      const u32x4* s = lds4 + buf * STAGE;
-      float sb[TN];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) sb[j] = SBg[(int64_t)sbrow[j] * nkb + kt];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        if (i >= tm_live) continue;
-        const int arow = (wm * TM + i) * 32 + lr;
-        // lanes 0-31 take chunks {0,1} then {4,5}; lanes 32-63 take {2,3} then {6,7}
-        const u32x4 a00 = s[arow * 8 + ((4 * 0 + 2 * hi + 0) ^ sw)];
-        const u32x4 a01 = s[arow * 8 + ((4 * 0 + 2 * hi + 1) ^ sw)];
-        const u32x4 a10 = s[arow * 8 + ((4 * 1 + 2 * hi + 0) ^ sw)];
-        const u32x4 a11 = s[arow * 8 + ((4 * 1 + 2 * hi + 1) ^ sw)];
-        float sa[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          sa[e] = sa_lds[buf * BM + (wm * TM + i) * 32 + 8 * (e >> 2) + 4 * hi + (e & 3)];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int brow = BM + bblock(j) * 32 + lr;
-          const u32x4 b00 = s[brow * 8 + ((2 * hi + 0) ^ sw)];
-          const u32x4 b01 = s[brow * 8 + ((2 * hi + 1) ^ sw)];
-          const u32x4 b10 = s[brow * 8 + ((4 + 2 * hi + 0) ^ sw)];
-          const u32x4 b11 = s[brow * 8 + ((4 + 2 * hi + 1) ^ sw)];
-          f32x16 part;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) part[e] = 0.0f;
-          part = mma_fp8(a00, a01, b00, b01, part);
-          part = mma_fp8(a10, a11, b10, b11, part);
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[i][j][e] += part[e] * (sa[e] * sb[j]);
-        }
-      }
-    }
-    if (kt + 1 < nkb) MOE_SSTORE(buf ^ 1);
-    __syncthreads();
-  }
-#undef MOE_GLOAD
-#undef MOE_SSTORE
-
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    if (i >= tm_live) continue;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int row = (wm * TM + i) * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
-      if (row >= rows) continue;
-      const int prow = r0 + row;
-      if constexpr (EPI == EPI_SWIGLU) {
-#pragma unroll
-        for (int j = 0; j < TN / 2; ++j) {
-          const int col = nt * (BN / 2) + (wn * (TN / 2) + j) * 32 + lr;
-          if (col < p.N)
-            ((uint16_t*)p.C)[(int64_t)prow * p.N + col] =
-                (uint16_t)f32_to_bf16_bits(silu_mul(acc[i][j][e], acc[i][j + TN / 2][e]));
-        }
-      } else if constexpr (EPI == EPI_SCATTER) {
-        const int tok = p.c_rows ? p.c_rows[prow] : prow;
-        const float w = p.row_w[prow];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int col = nt * BN + bblock(j) * 32 + lr;
-          if (col < p.N) atomicAdd((float*)p.C + (int64_t)tok * p.N + col, w * acc[i][j][e]);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int col = nt * BN + bblock(j) * 32 + lr;
-          if (col < p.N) ((uint16_t*)p.C)[(int64_t)prow * p.N + col] = (uint16_t)f32_to_bf16_bits(acc[i][j][e]);
-        }
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Pipelined FP8 kernel.  One K step = one 128-wide scale block = 128 bytes of
 // every A and B row, streamed straight into LDS rings (A: SA slots, B: SB slots)
@@ -602,8 +394,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_fp8_split_kernel(GemmFp8
         }
       }
       if (wn == 0 && hi == 0 && row < rows) {
-        if (p.cs_stride > 0) p.Cs[(int64_t)nt * p.cs_stride + r0 + row] = scale;  // k-block-major
-        else p.Cs[(int64_t)(r0 + row) * (p.N / 128) + nt] = scale;
+        p.Cs[(int64_t)nt * p.cs_stride + r0 + row] = scale;  // k-block-major
       }
     }
     __syncthreads();
@@ -703,53 +494,24 @@ static hipError_t launch8_split(const GemmFp8Params& p, int grid_m, hipStream_t 
   return hipGetLastError();
 }
 
-#ifndef MOE_TILE_FP8
-#define MOE_TILE_FP8 -1
-#endif
-
-// kind 0: register-staged 128 x 128 (any size); kind 1: pipelined 128 x 256
-// (A and B buffers addressed with 31-bit offsets), 2 x 4 waves of 64 x 64: two
-// waves per SIMD, so one wave's scaled fold (VALU) overlaps the other's MFMAs
-GemmShape gemm_fp8_shape(int rows_hint, int64_t a_bytes, int64_t b_bytes) {
+// kind 1: pipelined 128 x 256 (A and B buffers addressed with 31-bit offsets;
+// the ABI bounds both below 2^31 bytes), 2 x 4 waves of 64 x 64: two waves per
+// SIMD, so one wave's scaled fold (VALU) overlaps the other's MFMAs
+GemmShape gemm_fp8_shape() {
   GemmShape g;
-  (void)rows_hint;
-  const bool pipe_ok = a_bytes < (1LL << 31) && b_bytes < (1LL << 31);
-  g.kind = pipe_ok ? 1 : 0;
-  if (MOE_TILE_FP8 >= 0 && pipe_ok) g.kind = MOE_TILE_FP8;
+  g.kind = 1;
   g.bm = 128;
-  g.bn = g.kind == 0 ? 128 : 256;
+  g.bn = 256;
   return g;
 }
 
-template <int WM, int WN, int TM, int TN, int EPI>
-static hipError_t launch8(const GemmFp8Params& p, int grid_m, hipStream_t s) {
-  constexpr int BM = WM * TM * 32, BN = WN * TN * 32;
-  constexpr int lds_bytes = 2 * (BM + BN) * 128 + 2 * BM * 4;
-  auto kern = gemm_fp8_kernel<WM, WN, TM, TN, EPI>;
-  {
-    const hipError_t e = allow_lds<gemm_fp8_kernel<WM, WN, TM, TN, EPI>>(lds_bytes);
-    if (e != hipSuccess) return e;
-  }
-  const int64_t grid = (int64_t)grid_m * p.ntn;
-  if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WM * WN * 64), lds_bytes, s, p);
-  return hipGetLastError();
-}
-
 hipError_t launch_gemm_fp8(int epi, const GemmFp8Params& p, const GemmShape& g, int grid_m, hipStream_t s) {
-  if (g.kind == 1) {
-    if (epi == EPI_SWIGLU && (!p.Cq || !p.Cs)) return hipErrorInvalidValue;  // writes quantised h only
-    switch (epi) {
-      case EPI_SWIGLU: return launch8_split<2, 4, 2, 2, 3, 3, EPI_SWIGLU>(p, grid_m, s);
-      case EPI_SCATTER: return launch8_split<2, 4, 2, 2, 3, 3, EPI_SCATTER>(p, grid_m, s);
-      case EPI_STORE: return launch8_split<2, 4, 2, 2, 3, 3, EPI_STORE>(p, grid_m, s);
-      default: return hipErrorInvalidValue;
-    }
-  }
+  if (g.kind != 1) return hipErrorInvalidValue;
+  if (epi == EPI_SWIGLU && (!p.Cq || !p.Cs)) return hipErrorInvalidValue;  // writes quantised h only
   switch (epi) {
-    case EPI_SWIGLU: return launch8<2, 2, 2, 2, EPI_SWIGLU>(p, grid_m, s);
-    case EPI_SCATTER: return launch8<2, 2, 2, 2, EPI_SCATTER>(p, grid_m, s);
-    case EPI_STORE: return launch8<2, 2, 2, 2, EPI_STORE>(p, grid_m, s);
+    case EPI_SWIGLU: return launch8_split<2, 4, 2, 2, 3, 3, EPI_SWIGLU>(p, grid_m, s);
+    case EPI_SCATTER: return launch8_split<2, 4, 2, 2, 3, 3, EPI_SCATTER>(p, grid_m, s);
+    case EPI_STORE: return launch8_split<2, 4, 2, 2, 3, 3, EPI_STORE>(p, grid_m, s);
     default: return hipErrorInvalidValue;
   }
 }

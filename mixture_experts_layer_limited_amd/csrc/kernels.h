@@ -42,7 +42,7 @@ struct GemmShape {
   int kind = 0;
 };
 
-GemmShape gemm_shape(int which, int dt, int rows_hint, int64_t a_bytes, int64_t b_bytes);
+GemmShape gemm_shape(int which, int dt, int rows_hint);
 hipError_t launch_gemm(int dt, int epi, int odt, const GemmParams& p, const GemmShape& g, int grid_m,
                        hipStream_t s);
 // Pipelined bf16 kernel (LDS ring filled by direct-to-LDS buffer loads).
@@ -80,10 +80,10 @@ struct GemmFp8Params {
   int b2_group;
   int K;
   int N;
-  void* C;                // SwiGLU (kind 0): bf16 h [rows, N]; store: bf16 [rows, N]; scatter: fp32 [T, N]
-  uint8_t* Cq;            // SwiGLU (kind 1): E4M3 codes of h [rows, N] ...
-  float* Cs;              // ... and their 1x128 scales: Cs[kb * cs_stride + row] when cs_stride > 0,
-  int64_t cs_stride;      //     else Cs[row * (N / 128) + kb]
+  void* C;                // store: bf16 [rows, N]; scatter: fp32 [T, N]
+  uint8_t* Cq;            // SwiGLU: E4M3 codes of h [rows, N] ...
+  float* Cs;              // ... and their 1x128 scales, k-block-major: Cs[kb * cs_stride + row]
+  int64_t cs_stride;
   const int32_t* c_rows;
   const float* row_w;
   const int4* tiles;
@@ -93,7 +93,7 @@ struct GemmFp8Params {
   int ntn;
   int64_t a_nrows;        // rows of A and of its scales (bounds of the activation buffers)
 };
-GemmShape gemm_fp8_shape(int rows_hint, int64_t a_bytes, int64_t b_bytes);
+GemmShape gemm_fp8_shape();
 hipError_t launch_gemm_fp8(int epi, const GemmFp8Params& p, const GemmShape& g, int grid_m, hipStream_t s);
 
 // Grouped GEMM with 4-bit weights (two's-complement codes, two per byte, the
@@ -158,11 +158,13 @@ hipError_t launch_combine(int adt, int T, int H, int k, const void* expert_out, 
                           hipStream_t s);
 hipError_t launch_load_balance(const int32_t* offsets, int E, float* bias, float gamma, ::moe_load_stats* stats,
                                hipStream_t s);
-// scales [rows, cols/128], or k-block-major [cols/128, scales_t_stride] when scales_t_stride > 0
+// codes [rows, cols] E4M3, scales [rows, cols/128]
 hipError_t launch_quantize(int in_dt, int64_t rows, int64_t cols, const void* in, uint8_t* codes,
-                           float* scales, hipStream_t s, int64_t scales_t_stride = 0);
-// scales_t[kb * rows + p] = scales[src(p) * nkb + kb], src(p) = src[p] or p
-hipError_t launch_gather_scales_t(const float* scales, const int32_t* src, int64_t rows, int nkb, float* scales_t,
-                                  hipStream_t s);
+                           float* scales, hipStream_t s);
+// scales_t[kb * rows + p] = scales[src(p) * nkb + kb], src(p) = src[p] or p; a
+// row whose src(p) lies outside [0, src_rows) gets scale 1 (its activation
+// loads in the GEMM are out of range and read zeros)
+hipError_t launch_gather_scales_t(const float* scales, const int32_t* src, int64_t rows, int nkb,
+                                  int64_t src_rows, float* scales_t, hipStream_t s);
 
 }  // namespace moe

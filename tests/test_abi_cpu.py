@@ -61,6 +61,15 @@ def cfg(**kw):
     (dict(dtype="w4a16", shared_inter=2048 + 64), -3),
     (dict(n_experts=2048, n_group=8), -3),    # E > 1024
     (dict(top_k=33, topk_group=8), -3),       # k > 32
+    # one weight matrix past 2^31 bytes (32-bit buffer offsets in the GEMMs):
+    # bf16 w13 of 2 * 65536 * 8192 * 2 bytes = 2^31
+    (dict(hidden=8192, inter=65536, shared_inter=0), -3),
+    (dict(hidden=8192, inter=2048, shared_inter=65536), -3),      # the shared expert's
+    (dict(hidden=8192, inter=65536 - 64, shared_inter=0), 0),     # just below
+    (dict(dtype="fp8", hidden=8192, inter=131072, shared_inter=0), -3),   # E4M3: 1 byte a weight
+    (dict(dtype="fp8", hidden=8192, inter=65536, shared_inter=0), 0),
+    (dict(dtype="w4a16", hidden=8192, inter=262144, shared_inter=0), -3),  # 4-bit: half a byte
+    (dict(dtype="w4a16", hidden=8192, inter=131072, shared_inter=0), 0),
 ])
 def test_config_validation(kw, status):
     assert moe.validate_config(cfg(**kw)) == status

@@ -453,14 +453,26 @@ def test_staged_calls_match_forward():
 
 # ------------------------------------------------------ full-size workloads ---
 
-@pytest.mark.parametrize("name,samples", [("v2_lite_bf16", 8), ("v3_prefill_bf16", 6), ("v3_decode_bf16", 8),
-                                          ("v3_fp8", 4), ("v3_decode_w4a16", 8)])
-def test_forward_full_size_sampled(name, samples):
+FULL_SIZE = [
+    ("v2_lite_bf16", 8, moe.MOE_EPI_STORE_ROWS),
+    ("v3_prefill_bf16", 6, moe.MOE_EPI_STORE_ROWS),
+    ("v3_prefill_bf16", 6, moe.MOE_EPI_SCATTER_ADD),
+    ("v3_decode_bf16", 8, moe.MOE_EPI_STORE_ROWS),
+    ("v3_decode_bf16", 8, moe.MOE_EPI_SCATTER_ADD),
+    ("v3_fp8", 4, moe.MOE_EPI_STORE_ROWS),
+    ("v3_fp8", 4, moe.MOE_EPI_SCATTER_ADD),
+    ("v3_decode_w4a16", 8, moe.MOE_EPI_STORE_ROWS),
+]
+
+
+@pytest.mark.parametrize("name,samples,epi", FULL_SIZE)
+def test_forward_full_size_sampled(name, samples, epi):
     """The workload at its full size, in the launch configuration the
-    benchmark times: routing and permutation bit-exact on every token, layer
-    output on sampled tokens within tolerance."""
+    benchmark times (and with the scatter-add combine): routing and
+    permutation bit-exact on every token, layer output on sampled tokens
+    within tolerance."""
     cfg = PRESETS[name]
-    say(f"full-size forward {name} T={cfg.tokens}: drawing inputs")
+    say(f"full-size forward {name} T={cfg.tokens} epilogue={epi}: drawing inputs")
     inp = layer_inputs(cfg, 0, DEV)
     c = binding_config(cfg)
     T, E, k, H = cfg.tokens, cfg.n_experts, cfg.top_k, cfg.hidden
@@ -469,7 +481,8 @@ def test_forward_full_size_sampled(name, samples):
                              expert_offsets=i32(E + 1), permuted_src=i32(T * k), inv_perm=i32(T * k))
     say("  running the layer")
     moe.forward(c, T, inp["x"], inp["gate_w"], inp["bias"], inp["w13"], inp["w13_s"], inp["w2"], inp["w2_s"],
-                inp["sh_w13"], inp["sh_w13_s"], inp["sh_w2"], inp["sh_w2_s"], out, moe.workspace(c, T), aux=aux)
+                inp["sh_w13"], inp["sh_w13_s"], inp["sh_w2"], inp["sh_w2_s"], out, moe.workspace(c, T),
+                epilogue=epi, aux=aux)
     torch.cuda.synchronize()
     s_gpu = aux.scores.cpu().numpy()
     ids, w = oracle_routing(cfg, s_gpu, inp["bias"])
@@ -481,7 +494,7 @@ def test_forward_full_size_sampled(name, samples):
     assert np.array_equal(aux.inv_perm.cpu().numpy(), inv)
     st = oracle.load_stats(ids, E)
     say(f"  expert load: min {st['min']} max {st['max']} cv {st['cv']:.3f} empty {st['empty']}")
-    rng = np.random.default_rng(5)
+    rng = np.random.default_rng(5 + epi)
     toks = np.sort(rng.choice(T, size=samples, replace=False))
     say(f"  oracle on tokens {toks.tolist()}")
     ref = oracle_forward_rows(cfg, inp, ids, w, toks)
@@ -489,6 +502,73 @@ def test_forward_full_size_sampled(name, samples):
     say(f"  max rel err {err:.3e} (tol {TOL[cfg.dtype]})")
     assert err <= TOL[cfg.dtype]
     assert bool(torch.isfinite(out.float()).all())
+
+
+@pytest.mark.parametrize("name,n_top", [("v3_prefill_bf16", 3), ("v3_fp8", 2), ("v2_lite_bf16", 2)])
+def test_most_loaded_experts_every_row(name, n_top):
+    """Every row of the most-loaded experts at full size: these experts span
+    several m-tiles of the grouped GEMMs at the full K (two 256-row tiles at
+    V3 prefill and V2-Lite, four or five 128-row tiles at V3 FP8), so the
+    row split between m-tiles and the second tile's rows are all compared,
+    through the grouped SwiGLU call with stored rows."""
+    cfg = PRESETS[name]
+    say(f"most-loaded experts {name}: drawing inputs")
+    inp = layer_inputs(cfg, 0, DEV)
+    c = binding_config(cfg)
+    T, E, k, H = cfg.tokens, cfg.n_experts, cfg.top_k, cfg.hidden
+    scores, ids_d, w_d = f32((T, E)), i32((T, k)), f32((T, k))
+    moe.route(c, T, inp["x"], inp["gate_w"], inp["bias"], None, scores, ids_d, w_d,
+              moe.workspace(c, T, moe.MOE_OP_ROUTE))
+    off_d, src_d, inv_d = i32(E + 1), i32(T * k), i32(T * k)
+    moe.permute(c, T, ids_d, off_d, src_d, inv_d, moe.workspace(c, T, moe.MOE_OP_PERMUTE))
+    rows = torch.empty(T * k, H, dtype=torch.bfloat16, device=DEV)
+    moe.grouped_swiglu(c, T, inp["x"], None, src_d, off_d, inp["w13"], inp["w13_s"], inp["w2"], inp["w2_s"],
+                       moe.MOE_EPI_STORE_ROWS, None, None, rows, None,
+                       moe.workspace(c, T, moe.MOE_OP_GROUPED_SWIGLU))
+    torch.cuda.synchronize()
+    off, src = off_d.cpu().numpy().astype(np.int64), src_d.cpu().numpy().astype(np.int64)
+    counts = np.diff(off)
+    top = np.argsort(-counts, kind="stable")[:n_top]
+    say(f"  experts {top.tolist()} with {counts[top].tolist()} rows")
+    # the selected experts' rows as a small grouped problem of their own
+    sub_src = np.concatenate([src[off[e]:off[e + 1]] for e in top])
+    sub_off = np.concatenate([[0], np.cumsum(counts[top])])
+    x_sub = f64(inp["x"][torch.from_numpy(sub_src).to(DEV)])
+    exp = ExpertSource(inp, cfg.dtype)
+    qx, qh = fp8_quantizers(cfg)
+    ref = oracle.expert_outputs(x_sub, sub_off, np.arange(sub_src.size), lambda g: exp.expert(int(top[g])),
+                                qh, qx)
+    got = f64(torch.cat([rows[int(off[e]):int(off[e + 1])] for e in top]))
+    for g, e in enumerate(top):
+        lo, hi = int(sub_off[g]), int(sub_off[g + 1])
+        err = rel_err(got[lo:hi], ref[lo:hi])
+        say(f"  expert {int(e)}: {hi - lo} rows, max rel err {err:.3e} (tol {TOL[cfg.dtype]})")
+        assert err <= TOL[cfg.dtype]
+
+
+def test_fp8_hand_built_layer_is_exact():
+    """A one-token FP8 layer whose every intermediate value is exact (built
+    by hand in tests/test_oracle_fp8_layer.py, where the oracle is pinned to
+    it): the GPU must produce exactly 1, 28, 448, 28, 448 in columns 10, 11,
+    12, 20, 21 and zeros elsewhere.  It checks on the device what the CPU
+    test checks of the oracle: the router reads the raw x, the routed and the
+    shared experts read the 1x128-quantised x, and h is quantised after
+    SiLU(gate) * up."""
+    import test_oracle_fp8_layer as hand
+    x, gate_w, w13, w2, sh13, sh2 = hand._hand_layer()
+    H, I = hand.H, hand.I
+    enc = lambda a: torch.from_numpy(oracle.e4m3_encode(a)).to(DEV)
+    ones = lambda *shape: torch.ones(shape, dtype=torch.float32, device=DEV)
+    bf = lambda a: torch.from_numpy(a.astype(np.float32)).to(DEV).to(torch.bfloat16)
+    c = moe.make_config(hidden=H, inter=I, n_experts=2, top_k=1, shared_inter=hand.IS, scoring="softmax",
+                        norm_topk_prob=True, routed_scaling_factor=1.0, dtype="fp8")
+    out = torch.empty(1, H, dtype=torch.bfloat16, device=DEV)
+    aux = moe.ForwardOutputs(topk_ids=i32((1, 1)))
+    moe.forward(c, 1, bf(x), bf(gate_w), None, enc(w13), ones(2, 2, 1), enc(w2), ones(2, 1, 1), enc(sh13),
+                ones(2, 1), enc(sh2), ones(1, 1), out, moe.workspace(c, 1), aux=aux)
+    torch.cuda.synchronize()
+    assert aux.topk_ids.cpu().numpy().tolist() == [[1]]
+    np.testing.assert_array_equal(f64(out), hand._expected())
 
 
 # ----------------------------------------------------- load balance step ---
