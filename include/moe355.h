@@ -276,6 +276,32 @@ int moe_forward(const moe_config* cfg, int64_t T, const void* hidden, const void
                 const moe_forward_opts* opts, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * moe_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, results and launch sequence as moe_forward, without `ws`: the
+ * workspace is a static device buffer of MOE_STATIC_SCRATCH_BYTES inside the
+ * library, one copy per device, held until the process ends.  The call
+ * allocates nothing (no hipMalloc, no hipFree, no allocating library routine).
+ *   - a batch whose workspace (moe_workspace_size(cfg, T, MOE_OP_FORWARD) for
+ *     the epilogue in opts) exceeds MOE_STATIC_SCRATCH_BYTES is rejected with
+ *     MOE_ERR_WORKSPACE before anything touches the device; at V3 dimensions
+ *     (H 7168, E 256, I = Is = 2048, k 8) that allows T up to 256 in bf16;
+ *   - `stream` must belong to the current device (MOE_ERR_INVALID_ARG
+ *     otherwise); the buffer's device address is looked up once per device
+ *     (MOE_ERR_HIP if that fails);
+ *   - every call on one device shares that device's buffer: calls that
+ *     overlap on one device (other streams, other host threads) race, so
+ *     order them on one stream.  The buffer keeps the last call's contents;
+ *     the layer clears what it needs cleared with kernels of its own.
+ */
+#define MOE_STATIC_SCRATCH_BYTES (64u << 20)
+int moe_forward_static(const moe_config* cfg, int64_t T, const void* hidden, const void* gate_w,
+                       const float* bias, const void* w13, const float* w13_scales, const void* w2,
+                       const float* w2_scales, const void* sh_w13, const float* sh_w13_scales,
+                       const void* sh_w2, const float* sh_w2_scales, void* out,
+                       const moe_forward_opts* opts, hipStream_t stream);
+
+/*
  * Dynamic 1x128 E4M3 quantisation of activations (MoA routing + FP8
  * inference, blog.hotdry.top, FP8 section: 1x128 activation tiles; V3 lab
  * page §3 activation_scheme dynamic): per row and 128-column tile,

@@ -27,7 +27,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_CONFIG", -3: "MOE
           -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP"}
 
 EXPORTS = ("moe_workspace_size", "moe_validate_config", "moe_route", "moe_permute", "moe_grouped_swiglu",
-           "moe_combine", "moe_forward", "moe_load_balance", "moe_quantize_fp8_1x128",
+           "moe_combine", "moe_forward", "moe_forward_static", "moe_load_balance", "moe_quantize_fp8_1x128",
            "moe_strerror", "moe_version")
 
 
@@ -88,13 +88,15 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [cfgp, i64, vp, vp, vp, vp, vp, vp, vp]
         L.moe_forward.argtypes = [cfgp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                   ctypes.POINTER(ForwardOpts), vp, sz, vp]
+        L.moe_forward_static.argtypes = [cfgp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         ctypes.POINTER(ForwardOpts), vp]
         L.moe_load_balance.argtypes = [cfgp, vp, vp, ctypes.c_float, vp, vp]
         L.moe_quantize_fp8_1x128.argtypes = [i64, i64, vp, i32, vp, vp, vp]
         L.moe_strerror.argtypes = [ctypes.c_int]
         L.moe_strerror.restype = ctypes.c_char_p
         L.moe_version.argtypes = []
         for name in ("moe_validate_config", "moe_route", "moe_permute", "moe_grouped_swiglu", "moe_combine",
-                     "moe_forward", "moe_load_balance", "moe_quantize_fp8_1x128",
+                     "moe_forward", "moe_forward_static", "moe_load_balance", "moe_quantize_fp8_1x128",
                      "moe_version"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -187,6 +189,24 @@ def forward(cfg, T, hidden, gate_w, bias, w13, w13_scales, w2, w2_scales, sh_w13
                              _ptr(w13_scales), _ptr(w2), _ptr(w2_scales), _ptr(sh_w13), _ptr(sh_w13_scales),
                              _ptr(sh_w2), _ptr(sh_w2_scales), _ptr(out), ctypes.byref(opts), wp, wb,
                              _stream(stream)), "moe_forward")
+
+
+def forward_static(cfg, T, hidden, gate_w, bias, w13, w13_scales, w2, w2_scales, sh_w13, sh_w13_scales, sh_w2,
+                   sh_w2_scales, out, epilogue=MOE_EPI_STORE_ROWS, aux: Optional[ForwardOutputs] = None,
+                   stream=None):
+    """moe_forward_static: forward() with the library's static scratch instead of a workspace."""
+    aux = aux or ForwardOutputs()
+    ev = (ctypes.c_void_p * 4)(*[(aux.events[i] if aux.events and i < len(aux.events) else None)
+                                 for i in range(4)])
+    opts = ForwardOpts(epilogue, _ptr(aux.scores), _ptr(aux.topk_ids), _ptr(aux.topk_w), _ptr(aux.expert_offsets),
+                       _ptr(aux.permuted_src), _ptr(aux.inv_perm), ev)
+    _check(lib().moe_forward_static(ctypes.byref(cfg), T, _ptr(hidden), _ptr(gate_w), _ptr(bias), _ptr(w13),
+                                    _ptr(w13_scales), _ptr(w2), _ptr(w2_scales), _ptr(sh_w13), _ptr(sh_w13_scales),
+                                    _ptr(sh_w2), _ptr(sh_w2_scales), _ptr(out), ctypes.byref(opts),
+                                    _stream(stream)), "moe_forward_static")
+
+
+STATIC_SCRATCH_BYTES = 64 << 20   # MOE_STATIC_SCRATCH_BYTES of include/moe355.h
 
 
 class LoadStats(ctypes.Structure):

@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stddef.h>
 
+#include <mutex>
+
 #include "kernels.h"
 
 using namespace moe;
@@ -685,6 +687,72 @@ int moe_forward(const moe_config* c, int64_t T, const void* hidden, const void* 
   const void* shared_rows = merged ? (const void*)((const char*)w.y + rows * c->hidden * act_bytes(c)) : w.sh_out;
   HIP_TRY(launch_combine(act_dt(c), (int)T, c->hidden, c->top_k, w.y, w.acc, inv, topw, shared_rows, out, stream));
   return MOE_OK;
+}
+
+}  // extern "C"
+
+// --------------------------------------------- forward without allocation ---
+
+namespace {
+
+// The scratch of moe_forward_static: one copy on every device the library
+// runs on, held until the process ends.  Host code never passes `scratch`
+// itself to a kernel (on the host it names a stand-in, not device memory);
+// it uses the device address hipGetSymbolAddress returns for each device.
+static __device__ __align__(256) char scratch[MOE_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of this device's scratch, looked up once per device with
+// that device current.
+int scratch_for(int dev, void** ptr) {
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return MOE_ERR_HIP;
+    }
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward_static(const moe_config* c, int64_t T, const void* hidden, const void* gate_w, const float* bias,
+                       const void* w13, const float* w13_scales, const void* w2, const float* w2_scales,
+                       const void* sh_w13, const float* sh_w13_scales, const void* sh_w2, const float* sh_w2_scales,
+                       void* out, const moe_forward_opts* opts, hipStream_t stream) {
+  MOE_TRY(check_cfg(c));
+  MOE_TRY(check_T(c, T));
+  const int epi = opts ? opts->epilogue : MOE_EPI_STORE_ROWS;
+  if (epi != MOE_EPI_STORE_ROWS && epi != MOE_EPI_SCATTER_ADD) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return moe_forward(c, T, hidden, gate_w, bias, w13, w13_scales, w2, w2_scales, sh_w13, sh_w13_scales,
+                                 sh_w2, sh_w2_scales, out, opts, nullptr, 0, stream);
+  // The batch must fit the static scratch: rejected before touching the device.
+  Carver probe(nullptr);
+  ForwardWs w;
+  carve_forward(probe, c, T, epi == MOE_EPI_SCATTER_ADD, w);
+  if (probe.used > (size_t)MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  int cur = 0;
+  HIP_TRY(hipGetDevice(&cur));
+  if (stream) {
+    hipDevice_t sdev = 0;
+    HIP_TRY(hipStreamGetDevice(stream, &sdev));
+    if ((int)sdev != cur) return MOE_ERR_INVALID_ARG;
+  }
+  void* ws = nullptr;
+  MOE_TRY(scratch_for(cur, &ws));
+  return moe_forward(c, T, hidden, gate_w, bias, w13, w13_scales, w2, w2_scales, sh_w13, sh_w13_scales, sh_w2,
+                     sh_w2_scales, out, opts, ws, (size_t)MOE_STATIC_SCRATCH_BYTES, stream);
 }
 
 int moe_load_balance(const moe_config* c, const int32_t* expert_offsets, float* bias, float gamma,

@@ -158,6 +158,10 @@ def test_entry_points_reject_before_launch():
     assert L.moe_forward(b(c), 16, p, p, null, p, null, p, null, p, null, p, null, p, b(opts), p, 1 << 40,
                          null) == -1      # bad epilogue
     assert L.moe_forward(b(c), 16, p, p, null, p, null, p, null, p, null, p, null, p, null, p, 8, null) == -4
+    # the forward without a workspace: a batch past its static scratch, rejected before the device is touched
+    assert L.moe_forward_static(b(c), 4096, p, p, null, p, null, p, null, p, null, p, null, p, null, null) == -4
+    assert L.moe_forward_static(b(bad), 16, p, p, null, p, null, p, null, p, null, p, null, p, null, null) == -2
+    assert L.moe_forward_static(b(c), 0, p, p, null, p, null, p, null, p, null, p, null, p, null, null) == 0
     assert L.moe_load_balance(b(c), null, p, ctypes.c_float(0.01), p, null) == -1      # no offsets
     assert L.moe_load_balance(b(c), p, p, ctypes.c_float(-1.0), p, null) == -1        # negative step
     assert L.moe_load_balance(b(c), p, p, ctypes.c_float(float("nan")), p, null) == -1
