@@ -496,16 +496,25 @@ static hipError_t launch8_split(const GemmFp8Params& p, int grid_m, hipStream_t 
 
 // kind 1: pipelined 128 x 256 (A and B buffers addressed with 31-bit offsets;
 // the ABI bounds both below 2^31 bytes), 2 x 4 waves of 64 x 64: two waves per
-// SIMD, so one wave's scaled fold (VALU) overlaps the other's MFMAs
-GemmShape gemm_fp8_shape() {
+// SIMD, so one wave's scaled fold (VALU) overlaps the other's MFMAs.
+// kind 2: 256 x 256 (gemm_fp8_big.hip) for groups of 128 rows and more on
+// average, with the SwiGLU or row-store epilogue: half the weight-panel passes
+// per group.  The scatter-add epilogue keeps kind 1 (its fp32 atomics want
+// token rows first).
+#ifndef MOE_FP8_BIG_MIN_ROWS
+#define MOE_FP8_BIG_MIN_ROWS 128
+#endif
+GemmShape gemm_fp8_shape(int rows_hint, int epi) {
   GemmShape g;
-  g.kind = 1;
-  g.bm = 128;
+  const bool big = MOE_FP8_BIG_MIN_ROWS > 0 && rows_hint >= MOE_FP8_BIG_MIN_ROWS && epi != EPI_SCATTER;
+  g.kind = big ? 2 : 1;
+  g.bm = big ? 256 : 128;
   g.bn = 256;
   return g;
 }
 
 hipError_t launch_gemm_fp8(int epi, const GemmFp8Params& p, const GemmShape& g, int grid_m, hipStream_t s) {
+  if (g.kind == 2) return launch_gemm_fp8_big(epi, p, grid_m, s);
   if (g.kind != 1) return hipErrorInvalidValue;
   if (epi == EPI_SWIGLU && (!p.Cq || !p.Cs)) return hipErrorInvalidValue;  // writes quantised h only
   switch (epi) {

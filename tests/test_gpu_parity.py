@@ -257,6 +257,16 @@ SMALL = {
                                     shared_inter=256),
     "fp8_small": _reduced("v3_fp8", tokens=300, hidden=1024, inter=256, n_experts=64, shared_inter=256),
     "fp8_small_ragged": _reduced("v3_fp8", tokens=45, hidden=512, inter=384, n_experts=64, shared_inter=128),
+    # FP8 groups of ~275 rows: the 256-row FP8 tiles (two ragged m-tiles per expert), the
+    # shared expert of the routed width in its own dense launches (T > 1024)
+    "fp8_big": _reduced("v3_fp8", tokens=1100, hidden=512, inter=256, n_experts=16, n_group=4, topk_group=2,
+                        top_k=4, shared_inter=256),
+    # 256-row FP8 tiles with H a ragged number of 256-column n-tiles and I of 128-column ones
+    "fp8_big_ragged": _reduced("v3_fp8", tokens=777, hidden=640, inter=384, n_experts=8, n_group=1, topk_group=1,
+                               top_k=3, shared_inter=128),
+    # 256-row FP8 tiles, one group each (~250 rows: every token block of a tile live)
+    "fp8_big_full_tiles": _reduced("v3_fp8", tokens=500, hidden=768, inter=256, n_experts=8, n_group=1,
+                                   topk_group=1, top_k=4, shared_inter=256),
     # 4-bit weights: shared expert merged as one more group (Is == I, T <= 1024)
     "w4_small": _reduced("v3_decode_w4a16", tokens=300, hidden=1024, inter=256, n_experts=64, shared_inter=256,
                          bias="zero"),
@@ -374,32 +384,50 @@ def test_forward_zero_tokens_is_a_no_op():
     assert bool((out == 7.0).all())
 
 
-@pytest.mark.parametrize("mode", ["one_expert", "two_experts_empty_rest"])
-def test_grouped_swiglu_skewed(mode):
-    """All rows on one expert (many m-tiles of one group) and most experts empty."""
-    cfg = _reduced("v3_prefill_bf16", tokens=700, hidden=512, inter=384, n_experts=32, n_group=1, topk_group=1,
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("mode", ["one_expert", "two_experts_empty_rest", "mixed"])
+def test_grouped_swiglu_skewed(mode, dtype):
+    """All rows on one expert (many m-tiles of one group), most experts empty,
+    and a mix of group sizes whose tiles hold 1 to 16 token blocks (FP8: the
+    256-row tiles run every live-block count of their K loop)."""
+    base = "v3_prefill_bf16" if dtype == "bf16" else "v3_fp8"
+    cfg = _reduced(base, tokens=700, hidden=512, inter=384, n_experts=32, n_group=1, topk_group=1,
                    top_k=2, shared_inter=0)
-    say(f"grouped swiglu skew {mode}")
+    if mode == "mixed":
+        cfg = cfg.replace(n_experts=8)
+    say(f"grouped swiglu skew {mode} {dtype}")
     inp = layer_inputs(cfg, 1, DEV)
     T, E, k, H, I = cfg.tokens, cfg.n_experts, cfg.top_k, cfg.hidden, cfg.inter
     if mode == "one_expert":                       # every token: expert 3 plus one other
         other = np.arange(T) % (E - 1)
         ids = np.stack([np.full(T, 3), other + (other >= 3)], 1)
-    else:                                          # experts 5 and 9 only, 30 empty experts
+    elif mode == "two_experts_empty_rest":         # experts 5 and 9 only, 30 empty experts
         ids = np.tile(np.array([5, 9]), (T, 1))
+    else:                                          # 600, 300, 249, 130, 40, 37, 43 and 1 rows
+        first = np.concatenate([np.zeros(600), np.ones(100)]).astype(int)
+        second = np.concatenate([np.full(200, 1), np.full(249, 2), np.full(130, 3), np.full(40, 4),
+                                 np.full(37, 5), np.full(43, 6), np.full(1, 7)]).astype(int)
+        ids = np.stack([first, second], 1)
+        assert (ids[:, 0] != ids[:, 1]).all()
     c = binding_config(cfg)
     off, src, inv = oracle.permute(ids, E)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).astype(np.int32)).to(DEV)
     rows = torch.empty(T * k, H, dtype=torch.bfloat16, device=DEV)
     ws = moe.workspace(c, T, moe.MOE_OP_GROUPED_SWIGLU)
-    moe.grouped_swiglu(c, T, inp["x"], None, dev(src), dev(off), inp["w13"], None, inp["w2"], None,
+    moe.grouped_swiglu(c, T, inp["x"], None, dev(src), dev(off), inp["w13"], inp["w13_s"], inp["w2"], inp["w2_s"],
                        moe.MOE_EPI_STORE_ROWS, None, None, rows, None, ws)
     torch.cuda.synchronize()
-    srcx = ExpertSource(inp, "bf16")
-    ref = oracle.expert_outputs(f64(inp["x"]), off, src, srcx.expert)
+    srcx = ExpertSource(inp, cfg.dtype)
+    qx, qh = fp8_quantizers(cfg)
+    ref = oracle.expert_outputs(f64(inp["x"]), off, src, srcx.expert, qh, qx)
     err = rel_err(f64(rows), ref)
     say(f"  max rel err {err:.3e}")
-    assert err <= TOL["bf16"]
+    assert err <= TOL[cfg.dtype]
+    # every group on its own, so that a small group's error cannot hide under a large one's scale
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            assert rel_err(f64(rows[lo:hi]), ref[lo:hi]) <= TOL[cfg.dtype], e
 
 
 def test_shared_expert_through_grouped_call():
