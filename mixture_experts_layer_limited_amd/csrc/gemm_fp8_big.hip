@@ -235,16 +235,20 @@ __global__ __launch_bounds__(kBigNW * 64, 1) void gemm_fp8_big_kernel(GemmFp8Par
       wait_vm_barrier<VMN>();                                                                        \
       const char* sa_ = lds + sla * ASLOT;                                                           \
       const char* sb_ = lds + SA * ASLOT + slb * BSLOT;                                              \
+      /* reads in the order the first MFMAs consume them (LDS returns in order): */                   \
+      /* the first weight block, then the token blocks one by one */                                  \
       u32x4 ta[NL][2], wf[2][2];                                                                     \
-      _Pragma("unroll") for (int i = 0; i < NL; ++i) {                                               \
-        const char* r_ = sa_ + ((wm + WM * i) * 16 + lt) * ROW;                                      \
-        ta[i][0] = *(const u32x4*)(r_ + c0);                                                         \
-        ta[i][1] = *(const u32x4*)(r_ + c1);                                                         \
-      }                                                                                              \
       {                                                                                              \
         const char* r_ = sb_ + (wblock(0) * 16 + lt) * ROW;                                          \
         wf[0][0] = *(const u32x4*)(r_ + c0);                                                         \
         wf[0][1] = *(const u32x4*)(r_ + c1);                                                         \
+      }                                                                                              \
+      __builtin_amdgcn_sched_barrier(0);                                                             \
+      _Pragma("unroll") for (int i = 0; i < NL; ++i) {                                               \
+        const char* r_ = sa_ + ((wm + WM * i) * 16 + lt) * ROW;                                      \
+        ta[i][0] = *(const u32x4*)(r_ + c0);                                                         \
+        ta[i][1] = *(const u32x4*)(r_ + c1);                                                         \
+        __builtin_amdgcn_sched_barrier(0);                                                           \
       }                                                                                              \
       const int sla_n = sla ^ 1, slb_n2 = slb == 0 ? 2 : slb - 1; /* B slot of step kt + 2 */       \
       /* the next step's scales and A tile go out before any MFMA: the scales must */                 \
