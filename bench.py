@@ -110,12 +110,12 @@ def _blas_info():
     return int(threads), vendor
 
 
-def cpu_baseline(cfg, inp, min_seconds=10.0, max_experts=96):
+def cpu_baseline(cfg, inp, min_seconds=10.0, max_experts=None):
     """The fp64 oracle, as it stands, on a bounded sample shaped like the real
     batch.  Timed: routing and permutation of all T tokens (fp64 router GEMM,
     scoring, group-limited top-k); then, expert by expert in id order, the
     expert FFN over every row the expert received (its real row count) until
-    about min_seconds of work or max_experts experts; then the shared expert
+    about min_seconds of work (or max_experts experts); then the shared expert
     on the same number of tokens as the sample's routed rows / k.  Decoding the
     stored bf16 / E4M3 / 4-bit weights to fp64 is not timed.  The layer time
     is extrapolated per routed row (T*k rows) and per shared-expert token (T);
@@ -160,7 +160,7 @@ def cpu_baseline(cfg, inp, min_seconds=10.0, max_experts=96):
         rows += hi - lo
         n_exp += 1
         flops += 6.0 * (hi - lo) * H * I
-        if t_route + t_exp >= 0.8 * min_seconds or n_exp >= max_experts:
+        if t_route + t_exp >= 0.8 * min_seconds or (max_experts is not None and n_exp >= max_experts):
             break
     n_sh, t_sh = 0, 0.0
     if Is > 0:
@@ -182,6 +182,47 @@ def cpu_baseline(cfg, inp, min_seconds=10.0, max_experts=96):
                        + ("" if whole else "; layer time extrapolated per routed row and per shared token"))}
 
 
+def oracle_check(cfg, inp, routing, out, samples=4):
+    """Part of the oracle leg, outside any timed region: the benchmarked
+    forward's routing and permutation against the oracle's selection from the
+    same fp32 score tensor (bit-exact), and its output rows on a few sampled
+    tokens against the oracle's fp64 layer (max |got - ref| / max |ref|)."""
+    import numpy as np
+    import oracle
+
+    bias = None if inp["bias"] is None else inp["bias"].float().cpu().numpy()
+    s = routing["scores"]
+    ids = oracle.select_experts(s.astype(np.float32), bias, cfg.top_k, cfg.n_group, cfg.topk_group, dtype=np.float32)
+    w = oracle.routing_weights(s, ids, cfg.norm_topk_prob, cfg.routed_scaling_factor)
+    off, src, inv = oracle.permute(ids, cfg.n_experts)
+    routing_exact = bool(np.array_equal(routing["topk_ids"], ids))
+    perm_exact = bool(np.array_equal(routing["expert_offsets"], off) and np.array_equal(routing["permuted_src"], src)
+                      and np.array_equal(routing["inv_perm"], inv))
+    fp8 = cfg.dtype == "fp8"
+    scaled = cfg.dtype in ("fp8", "w4a16")
+
+    def dec(name, e=None):
+        t = inp[name] if e is None else inp[name][e]
+        if not scaled:
+            return t.float().cpu().double().numpy()
+        sc = (inp[name + "_s"] if e is None else inp[name + "_s"][e]).cpu().numpy()
+        if fp8:
+            return oracle.dequantize_blocks(t.cpu().numpy(), sc)
+        return oracle.dequantize_int4_groups(t.cpu().numpy(), sc)
+
+    rng = np.random.default_rng(11)
+    toks = np.sort(rng.choice(cfg.tokens, size=min(samples, cfg.tokens), replace=False))
+    q = oracle.quantize_dequantize_1x128 if fp8 else None
+    shared = (lambda: (dec("sh_w13"), dec("sh_w2"))) if cfg.shared_inter > 0 else None
+    ref = oracle.moe_layer_rows(toks, inp["x"].float().cpu().double().numpy(), ids, w,
+                                lambda e: (dec("w13", e), dec("w2", e)), shared, quantize_x=q, quantize_h=q)
+    got = out[toks].float().cpu().double().numpy()
+    err = float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
+    tol = {"f32": 1e-4, "bf16": 1e-2, "fp8": 3e-2, "w4a16": 1e-2}[cfg.dtype]
+    return {"routing_bit_exact": routing_exact, "permutation_bit_exact": perm_exact,
+            "sampled_tokens": [int(t) for t in toks], "max_rel_err": err, "tol": tol, "within_tol": err <= tol}
+
+
 def time_layer(moe, torch, np, cfg, inp, epilogue, steps, warmup):
     """Warm-up, then `steps` timed forwards of the layer: the region's mean per
     forward, every forward's own time, and the routed gate/up and down GEMMs'
@@ -197,14 +238,23 @@ def time_layer(moe, torch, np, cfg, inp, epilogue, steps, warmup):
     ws = moe.workspace(c, T, device=dev)
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
 
-    def step(events=None):
+    def step(events=None, aux=None):
         moe.forward(c, T, inp["x"], inp["gate_w"], inp["bias"], inp["w13"], inp["w13_s"], inp["w2"], inp["w2_s"],
                     inp["sh_w13"], inp["sh_w13_s"], inp["sh_w2"], inp["sh_w2_s"], out, ws, epilogue=epi,
-                    aux=moe.ForwardOutputs(expert_offsets=offsets, events=events))
+                    aux=aux or moe.ForwardOutputs(expert_offsets=offsets, events=events))
 
-    step()
+    # first (untimed) call: the routing and permutation of this batch, for the load summary and the checks
+    k = cfg.top_k
+    first = moe.ForwardOutputs(scores=torch.empty(T, E, dtype=torch.float32, device=dev),
+                               topk_ids=torch.empty(T, k, dtype=torch.int32, device=dev),
+                               topk_w=torch.empty(T, k, dtype=torch.float32, device=dev), expert_offsets=offsets,
+                               permuted_src=torch.empty(T * k, dtype=torch.int32, device=dev),
+                               inv_perm=torch.empty(T * k, dtype=torch.int32, device=dev))
+    step(aux=first)
     torch.cuda.synchronize()
-    counts = np.diff(offsets.cpu().numpy())
+    routing = {f: getattr(first, f).cpu().numpy() for f in ("scores", "topk_ids", "topk_w", "expert_offsets",
+                                                            "permuted_src", "inv_perm")}
+    counts = np.diff(routing["expert_offsets"]).astype(np.float64)
     non_empty = int((counts > 0).sum())
     for _ in range(warmup):
         step()
@@ -222,7 +272,10 @@ def time_layer(moe, torch, np, cfg, inp, epilogue, steps, warmup):
     g1 = float(np.mean([ev.ms(ev.ev[4 * i], ev.ev[4 * i + 1]) for i in range(steps)]))
     g2 = float(np.mean([ev.ms(ev.ev[4 * i + 2], ev.ev[4 * i + 3]) for i in range(steps)]))
     ev.close()
-    return ms, per_step, g1, g2, non_empty
+    load = {"min": int(counts.min()), "max": int(counts.max()), "mean": float(counts.mean()),
+            "cv": float(counts.std(ddof=1) / counts.mean()) if counts.size > 1 and counts.mean() > 0 else 0.0,
+            "empty": int((counts == 0).sum())}
+    return ms, per_step, g1, g2, non_empty, load, routing, out
 
 
 def work(cfg, epilogue, non_empty):
@@ -262,7 +315,7 @@ def decode_object(moe, torch, np, layer_inputs, PRESETS, steps, warmup):
     cfg = PRESETS["v3_decode_bf16"]
     print(f"[bench] drawing inputs for {cfg.name}", file=sys.stderr, flush=True)
     inp = layer_inputs(cfg, 0, "cuda")
-    ms, per_step, g1, g2, non_empty = time_layer(moe, torch, np, cfg, inp, "store", steps, warmup)
+    ms, per_step, g1, g2, non_empty, load, _, _ = time_layer(moe, torch, np, cfg, inp, "store", steps, warmup)
     w = work(cfg, "store", non_empty)
     gemm_bytes = w["bytes1"] + w["bytes2"]
     del inp
@@ -271,7 +324,7 @@ def decode_object(moe, torch, np, layer_inputs, PRESETS, steps, warmup):
                         f"k={cfg.top_k} groups {cfg.n_group}/{cfg.topk_group} sigmoid + Zipf(1.1)-calibrated bias, "
                         f"shared Is={cfg.shared_inter}, bf16",
             "steps": steps, "warmup": warmup, "ms_per_step": ms, "tokens_per_s": cfg.tokens / (ms * 1e-3),
-            "step_ms_median": float(np.median(per_step)), "non_empty_experts": non_empty,
+            "step_ms_median": float(np.median(per_step)), "non_empty_experts": non_empty, "expert_load": load,
             "layer_bytes": w["layer_bytes"], "layer_gb_s": w["layer_bytes"] / (ms * 1e-3) / 1e9,
             "layer_hbm_frac": w["layer_bytes"] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "ms_gate_up": g1, "ms_down": g2, "grouped_gemm_bytes": gemm_bytes,
@@ -297,7 +350,8 @@ def main():
     print(f"[bench] drawing inputs for {cfg.name} on {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
     inp = layer_inputs(cfg, 0, "cuda")
     T, E, k, H, I, Is = cfg.tokens, cfg.n_experts, cfg.top_k, cfg.hidden, cfg.inter, cfg.shared_inter
-    ms, per_step, g1, g2, non_empty = time_layer(moe, torch, np, cfg, inp, a.epilogue, a.steps, a.warmup)
+    ms, per_step, g1, g2, non_empty, load, routing, out = time_layer(moe, torch, np, cfg, inp, a.epilogue, a.steps,
+                                                                      a.warmup)
     w = work(cfg, a.epilogue, non_empty)
     flops1, flops2, bytes1, bytes2, merged = w["flops1"], w["flops2"], w["bytes1"], w["bytes2"], w["merged"]
     peak = PEAK_TFLOPS[cfg.dtype]
@@ -336,7 +390,7 @@ def main():
                    "inter": I, "top_k": k, "shared_inter": Is, "epilogue": a.epilogue,
                    "expert_weights": {"f32": "fp32", "bf16": "bf16", "fp8": "E4M3 + 128x128 fp32 scales",
                                       "w4a16": "int4 + fp32 scale per row and 128 columns, bf16 MFMAs"}[cfg.dtype],
-                   "non_empty_experts": non_empty},
+                   "non_empty_experts": non_empty, "expert_load": load},
         "grouped_gemm": {"ms_gate_up": g1, "ms_down": g2, "shared_expert_included": merged,
                          "tflops": gg_tflops, "peak_tflops": peak,
                          "frac_mfma_peak": gg_tflops / peak,
@@ -346,6 +400,7 @@ def main():
     if a.cpu_seconds > 0:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, inp, min_seconds=a.cpu_seconds)
+        result["cpu_baseline"]["check"] = oracle_check(cfg, inp, routing, out)
     if a.config == "v3_prefill_bf16" and a.decode_steps > 0:
         del inp
         torch.cuda.empty_cache()

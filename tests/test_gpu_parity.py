@@ -670,11 +670,14 @@ def test_forward_is_deterministic(name):
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
+@pytest.mark.parametrize("entry", ["forward", "forward_static"])
 @pytest.mark.parametrize("name", ["v3_small", "fp8_small", "w4_small"])
-def test_forward_in_a_hip_graph(name):
+def test_forward_in_a_hip_graph(name, entry):
     """moe_forward allocates nothing and never synchronises, so a whole layer can
     be captured into a HIP graph: every replay, with eager work in between,
-    equals the eager forward."""
+    equals the eager forward.  The same holds for moe_forward_static, whose
+    scratch is the library's own static buffer (the caller it serves is code
+    under graph capture)."""
     cfg = SMALL[name]
     inp = layer_inputs(cfg, 5, DEV)
     c = binding_config(cfg)
@@ -682,6 +685,11 @@ def test_forward_in_a_hip_graph(name):
     ws = moe.workspace(c, T)
     args = (inp["x"], inp["gate_w"], inp["bias"], inp["w13"], inp["w13_s"], inp["w2"], inp["w2_s"],
             inp["sh_w13"], inp["sh_w13_s"], inp["sh_w2"], inp["sh_w2_s"])
+    if entry == "forward":
+        run = lambda o: moe.forward(c, T, *args, o, ws)
+    else:
+        assert moe.workspace_size(c, T) <= moe.STATIC_SCRATCH_BYTES
+        run = lambda o: moe.forward_static(c, T, *args, o)
     ref = torch.empty(T, H, dtype=inp["x"].dtype, device=DEV)
     moe.forward(c, T, *args, ref, ws)
     torch.cuda.synchronize()
@@ -689,12 +697,12 @@ def test_forward_in_a_hip_graph(name):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):                      # warm-up on the capture stream
-        moe.forward(c, T, *args, out, ws)
+        run(out)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        moe.forward(c, T, *args, out, ws)
+        run(out)
     for rep in range(3):
         out.zero_()
         noise = torch.randn(1 << 20, device=DEV).sum()  # eager work between replays
