@@ -12,7 +12,7 @@
 // (2 per SIMD, 128 accumulator registers each), so the per-block scale fold
 // must not keep a partial per accumulator: each 16 x 16 block's K step is ONE
 // v_mfma 16x16x128 (the whole 128-wide scale block) into a fresh partial, and
-// the partial folds into the accumulator two MFMAs later, with the product of
+// the partial folds into the accumulator three MFMAs later, with the product of
 // the token's activation scale and the block's weight scale.
 //
 // Blocks run transposed: weight rows are the MFMA's first operand, so a lane's
@@ -65,6 +65,10 @@ __global__ __launch_bounds__(kBigNW * 64, 1) void gemm_fp8_big_kernel(GemmFp8Par
   constexpr int AI = BM / RPI / NW, BI = BN / RPI / NW;  // ring DMAs per wave per step (4 + 4)
   // at the top of step kt only B(kt+1) (issued last in step kt-1) may be in flight
   constexpr int VMN = BI;
+  // partials in flight: MFMA q is folded NP - 1 MFMAs later, past the MFMA
+  // pipeline latency (with NP = 3 the fold waited on it)
+  constexpr int NP = 4;
+  static_assert(NP == 4, "the K loop folds the last three partials by name");
   static_assert(AI * RPI * NW == BM && BI * RPI * NW == BN, "tile / wave mismatch");
 
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -216,18 +220,18 @@ __global__ __launch_bounds__(kBigNW * 64, 1) void gemm_fp8_big_kernel(GemmFp8Par
     su_[i] = sa_n[i] * sb_n[1];
   }
 
-  // Fold of the partial of MFMA q (block i = q % NL, j = q / NL), in slot q % 3.
+  // Fold of the partial of MFMA q (block i = q % NL, j = q / NL), in slot q % NP.
 #define MOE_BIG_FOLD(q)                                                                              \
   do {                                                                                               \
     const int fj_ = (q) / NL, fi_ = (q) % NL;                                                        \
     const float sc_ = (EPI != EPI_SWIGLU || fj_ < TN / 2) ? sg_[fi_] : su_[fi_];                     \
-    acc[fi_][fj_] += pt_[(q) % 3] * sc_;                                                             \
+    acc[fi_][fj_] += pt_[(q) % NP] * sc_;                                                            \
   } while (0)
 
   // The K loop, one 128-wide scale block per step.  Ring slots are wave-uniform
   // counters (A: kt % 2, B: kt % 3).  Per weight block j: its fragment (read one
   // block ahead), NL MFMAs (one per live token block), and the fold of the
-  // partial two MFMAs back.
+  // partial three MFMAs back.
 #define MOE_BIG_KLOOP                                                                                \
   {                                                                                                  \
     int sla = 0, slb = 0;                                                                            \
@@ -256,7 +260,7 @@ __global__ __launch_bounds__(kBigNW * 64, 1) void gemm_fp8_big_kernel(GemmFp8Par
       MOE_BIG_LOAD_SCALES(kt + 1);                                                                   \
       MOE_BIG_ISSUE_A(kt + 1, sla_n);                                                                \
       __builtin_amdgcn_sched_barrier(0);                                                             \
-      f32x4 pt_[3];                                                                                  \
+      f32x4 pt_[NP];                                                                                 \
       _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                               \
         if (j + 1 < TN) {                                                                            \
           const char* r_ = sb_ + (wblock(j + 1) * 16 + lt) * ROW;                                    \
@@ -267,10 +271,12 @@ __global__ __launch_bounds__(kBigNW * 64, 1) void gemm_fp8_big_kernel(GemmFp8Par
         if (j == 3) MOE_BIG_ISSUE_B(kt + SB - 1, slb_n2, BI / 2, BI);                                \
         _Pragma("unroll") for (int i = 0; i < NL; ++i) {                                             \
           const int q_ = j * NL + i;                                                                 \
-          if (q_ >= 2) MOE_BIG_FOLD(q_ - 2);                                                         \
-          pt_[q_ % 3] = mma16_fp8(wf[j & 1][0], wf[j & 1][1], ta[i][0], ta[i][1]);                   \
+          if (q_ >= NP - 1) MOE_BIG_FOLD(q_ - NP + 1);                                               \
+          pt_[q_ % NP] = mma16_fp8(wf[j & 1][0], wf[j & 1][1], ta[i][0], ta[i][1]);                   \
+          __builtin_amdgcn_sched_barrier(0); /* keeps each fold NP - 1 MFMAs behind */             \
         }                                                                                            \
       }                                                                                              \
+      MOE_BIG_FOLD(NL * TN - 3);                                                                     \
       MOE_BIG_FOLD(NL * TN - 2);                                                                     \
       MOE_BIG_FOLD(NL * TN - 1);                                                                     \
       _Pragma("unroll") for (int i = 0; i < NL; ++i) {                                               \
