@@ -150,17 +150,21 @@ void carve_permute(Carver& cv, const moe_config* c, int64_t T, PermuteWs& w) {
 }
 
 // Tile shapes of the gate/up and down GEMMs of one grouped SwiGLU.
-GemmShape shape1(const moe_config* c, int64_t rows, int groups) {
-  return gemm_shape(0, act_dt(c), (int)(rows / groups));
+// A dense call (one group) passes its 256 x 256 tile count, so that a launch
+// too small to fill the chip can take smaller tiles.
+GemmShape shape1(const moe_config* c, int64_t rows, int groups, int I) {
+  const int64_t t256 = groups == 1 ? ((rows + 255) / 256) * ntiles_n(I, 128) : 0;
+  return gemm_shape(0, act_dt(c), (int)(rows / groups), t256);
 }
 GemmShape shape2(const moe_config* c, int64_t rows, int groups) {
-  return gemm_shape(1, act_dt(c), (int)(rows / groups));
+  const int64_t t256 = groups == 1 ? ((rows + 255) / 256) * ntiles_n(c->hidden, 256) : 0;
+  return gemm_shape(1, act_dt(c), (int)(rows / groups), t256);
 }
 
-GemmShape tile_shape1(const moe_config* c, int64_t rows, int groups) {
+GemmShape tile_shape1(const moe_config* c, int64_t rows, int groups, int I) {
   if (is_fp8(c)) return gemm_fp8_shape((int)(rows / groups), EPI_SWIGLU);
   if (is_w4(c)) return gemm_w4_shape();
-  return shape1(c, rows, groups);
+  return shape1(c, rows, groups, I);
 }
 GemmShape tile_shape2(const moe_config* c, int64_t rows, int groups, bool scatter) {
   if (is_fp8(c)) return gemm_fp8_shape((int)(rows / groups), scatter ? EPI_SCATTER : EPI_STORE);
@@ -181,7 +185,7 @@ struct SwigluWs {
 };
 void carve_swiglu(Carver& cv, const moe_config* c, int64_t T, int64_t rows, int groups, int I,
                   bool quantize_x, bool scatter, SwigluWs& w) {
-  const GemmShape g1 = tile_shape1(c, rows, groups);
+  const GemmShape g1 = tile_shape1(c, rows, groups, I);
   const GemmShape g2 = tile_shape2(c, rows, groups, scatter);
   // tile lists: every (m-tile, n-tile) pair of the gate/up and of the down GEMM
   w.tiles1 = cv.take<int4>((size_t)max_mtiles(rows, g1.bm, groups) * ntiles_n(I, g1.bn / 2) + 1);
@@ -340,7 +344,7 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
       HIP_TRY(launch_quantize(act_dt(c), T, H, hidden, w.xq, w.xs, s));
       xq = w.xq; xs = w.xs;
     }
-    const GemmShape g1 = tile_shape1(c, rows, groups);
+    const GemmShape g1 = tile_shape1(c, rows, groups, I);
     const GemmShape g2 = tile_shape2(c, rows, groups, epi == MOE_EPI_SCATTER_ADD);
     const bool dense = offsets == nullptr;
     const int ntn1 = ntiles_n(I, g1.bn / 2), ntn2 = ntiles_n(H, g2.bn);
@@ -430,7 +434,7 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
     return mark(3);
   }
   const int dt = act_dt(c);
-  const GemmShape g1 = shape1(c, rows, groups);
+  const GemmShape g1 = shape1(c, rows, groups, I);
   const GemmShape g2 = shape2(c, rows, groups);
   const bool dense = offsets == nullptr;
   const int ntn1 = ntiles_n(I, g1.bn / 2), ntn2 = ntiles_n(H, g2.bn);
@@ -646,7 +650,7 @@ int moe_forward(const moe_config* c, int64_t T, const void* hidden, const void* 
   // Small batches: the permutation's one work-group also writes both GEMMs' tile
   // lists (when their m-tiles have one height).
   const int groups = E + (merged ? 1 : 0);
-  const GemmShape g1 = tile_shape1(c, rows_all, groups);
+  const GemmShape g1 = tile_shape1(c, rows_all, groups, c->inter);
   const GemmShape g2 = tile_shape2(c, rows_all, groups, scatter);
   TileLists tl;
   if (g1.bm == g2.bm) {

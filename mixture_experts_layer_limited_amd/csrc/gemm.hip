@@ -274,15 +274,19 @@ static int tile_bm(int kind) {
 static int tile_bn(int kind) { return kind == 0 ? 128 : 256; }
 
 // which: 0 = gate/up GEMM, 1 = down GEMM, 2 = router GEMM.  rows_hint = mean
-// rows per group.  bf16 always takes a pipelined kernel (the ABI bounds the
+// rows per group; tiles256 = the launch's work-groups with 256 x 256 tiles
+// (0: not known).  bf16 always takes a pipelined kernel (the ABI bounds the
 // activation buffers and every weight matrix below 2^31 bytes, the reach of its
 // 32-bit buffer offsets); fp32 takes the register-staged one.
-GemmShape gemm_shape(int which, int dt, int rows_hint) {
+GemmShape gemm_shape(int which, int dt, int rows_hint, int64_t tiles256) {
   int kind;
   if (dt != MOE_DT_BF16) kind = (which != 2 && rows_hint <= 32) ? 1 : 0;
   else if (which == 2) kind = 14;  // router: 64 x 256 tiles, split K
   else if (rows_hint <= 32) kind = which == 1 ? 13 : 14;
   else if (rows_hint < 128) kind = 12;
+  // a launch with fewer 256 x 256 tiles than the chip has CUs leaves CUs idle
+  // (one work-group per CU): 128 x 256 tiles double its work-groups
+  else if (tiles256 > 0 && tiles256 < kChipCUs) kind = 12;
   else kind = 15;
   if (dt == MOE_DT_BF16) {
     if (which == 0 && MOE_TILE_GEMM1 >= 12 && MOE_TILE_GEMM1 <= 15) kind = MOE_TILE_GEMM1;

@@ -42,7 +42,9 @@ struct GemmShape {
   int kind = 0;
 };
 
-GemmShape gemm_shape(int which, int dt, int rows_hint);
+// MI355X: 256 compute units.
+constexpr int kChipCUs = 256;
+GemmShape gemm_shape(int which, int dt, int rows_hint, int64_t tiles256 = 0);
 hipError_t launch_gemm(int dt, int epi, int odt, const GemmParams& p, const GemmShape& g, int grid_m,
                        hipStream_t s);
 // Pipelined bf16 kernel (LDS ring filled by direct-to-LDS buffer loads).
