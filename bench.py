@@ -69,7 +69,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="v3_prefill_bf16")
     p.add_argument("--epilogue", choices=["store", "scatter"], default="store")
-    p.add_argument("--cpu-seconds", type=float, default=10.0,
+    p.add_argument("--cpu-seconds", type=float, default=12.5,
                    help="about this much timed host work for the oracle's sample (0 = skip)")
     p.add_argument("--decode-steps", type=int, default=200,
                    help="timed forwards of the V3 decode layer reported beside the default workload (0 = skip)")
