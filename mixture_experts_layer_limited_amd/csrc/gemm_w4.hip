@@ -296,17 +296,22 @@ __global__ __launch_bounds__(512, 1) void gemm_w4_kernel(GemmW4Params p) {
                                                        __builtin_bit_cast(bf16x8, kneg), base, 0, 0, 0);
 #pragma unroll
       for (int st = 0; st < 4; ++st) a[st] = reorder_a(a[st]);
+      // the NB chains run interleaved (sub-step outer), so consecutive MFMAs
+      // do not wait on each other; each chain keeps its own order
+      f32x4 part[NB];
 #pragma unroll
-      for (int jb = 0; jb < NB; ++jb) {
-        f32x4 part = base;
+      for (int jb = 0; jb < NB; ++jb) part[jb] = base;
 #pragma unroll
-        for (int st = 0; st < 4; ++st)
-          part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[st]),
-                                                         __builtin_bit_cast(bf16x8, widen_w4(b[jb][st])), part, 0,
-                                                         0, 0);
+      for (int st = 0; st < 4; ++st)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[jb][r] = fmaf(sc[jb], part[r], acc[jb][r]);
-      }
+        for (int jb = 0; jb < NB; ++jb)
+          part[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[st]),
+                                                             __builtin_bit_cast(bf16x8, widen_w4(b[jb][st])),
+                                                             part[jb], 0, 0, 0);
+#pragma unroll
+      for (int jb = 0; jb < NB; ++jb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[jb][r] = fmaf(sc[jb], part[jb][r], acc[jb][r]);
     }
     after_epi = false;
     if (++c_k < nk) continue;
