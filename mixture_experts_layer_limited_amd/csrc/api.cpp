@@ -162,12 +162,12 @@ GemmShape shape2(const moe_config* c, int64_t rows, int groups) {
 }
 
 GemmShape tile_shape1(const moe_config* c, int64_t rows, int groups, int I) {
-  if (is_fp8(c)) return gemm_fp8_shape((int)(rows / groups), EPI_SWIGLU);
+  if (is_fp8(c)) return gemm_fp8_shape((int)(rows / groups), EPI_SWIGLU, c->hidden);
   if (is_w4(c)) return gemm_w4_shape();
   return shape1(c, rows, groups, I);
 }
-GemmShape tile_shape2(const moe_config* c, int64_t rows, int groups, bool scatter) {
-  if (is_fp8(c)) return gemm_fp8_shape((int)(rows / groups), scatter ? EPI_SCATTER : EPI_STORE);
+GemmShape tile_shape2(const moe_config* c, int64_t rows, int groups, int I, bool scatter) {
+  if (is_fp8(c)) return gemm_fp8_shape((int)(rows / groups), scatter ? EPI_SCATTER : EPI_STORE, I);
   if (is_w4(c)) return gemm_w4_shape();
   return shape2(c, rows, groups);
 }
@@ -186,7 +186,7 @@ struct SwigluWs {
 void carve_swiglu(Carver& cv, const moe_config* c, int64_t T, int64_t rows, int groups, int I,
                   bool quantize_x, bool scatter, SwigluWs& w) {
   const GemmShape g1 = tile_shape1(c, rows, groups, I);
-  const GemmShape g2 = tile_shape2(c, rows, groups, scatter);
+  const GemmShape g2 = tile_shape2(c, rows, groups, I, scatter);
   // tile lists: every (m-tile, n-tile) pair of the gate/up and of the down GEMM
   w.tiles1 = cv.take<int4>((size_t)max_mtiles(rows, g1.bm, groups) * ntiles_n(I, g1.bn / 2) + 1);
   w.ntiles1 = cv.take<int>(1);
@@ -345,7 +345,7 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
       xq = w.xq; xs = w.xs;
     }
     const GemmShape g1 = tile_shape1(c, rows, groups, I);
-    const GemmShape g2 = tile_shape2(c, rows, groups, epi == MOE_EPI_SCATTER_ADD);
+    const GemmShape g2 = tile_shape2(c, rows, groups, I, epi == MOE_EPI_SCATTER_ADD);
     const bool dense = offsets == nullptr;
     const int ntn1 = ntiles_n(I, g1.bn / 2), ntn2 = ntiles_n(H, g2.bn);
     if (!dense && !tiles_ready) {
@@ -651,7 +651,7 @@ int moe_forward(const moe_config* c, int64_t T, const void* hidden, const void* 
   // lists (when their m-tiles have one height).
   const int groups = E + (merged ? 1 : 0);
   const GemmShape g1 = tile_shape1(c, rows_all, groups, c->inter);
-  const GemmShape g2 = tile_shape2(c, rows_all, groups, scatter);
+  const GemmShape g2 = tile_shape2(c, rows_all, groups, c->inter, scatter);
   TileLists tl;
   if (g1.bm == g2.bm) {
     tl.bm = g1.bm;

@@ -504,9 +504,12 @@ static hipError_t launch8_split(const GemmFp8Params& p, int grid_m, hipStream_t 
 #ifndef MOE_FP8_BIG_MIN_ROWS
 #define MOE_FP8_BIG_MIN_ROWS 128
 #endif
-GemmShape gemm_fp8_shape(int rows_hint, int epi) {
+GemmShape gemm_fp8_shape(int rows_hint, int epi, int K) {
   GemmShape g;
-  const bool big = MOE_FP8_BIG_MIN_ROWS > 0 && rows_hint >= MOE_FP8_BIG_MIN_ROWS && epi != EPI_SCATTER;
+  // the 256 x 256 kernel keeps a tile's weight-block scales in one register
+  // per wave (one 128-wide K step per lane): K <= 64 * 128
+  const bool big = MOE_FP8_BIG_MIN_ROWS > 0 && rows_hint >= MOE_FP8_BIG_MIN_ROWS && epi != EPI_SCATTER &&
+                   K <= kFp8BigMaxK;
   g.kind = big ? 2 : 1;
   g.bm = big ? 256 : 128;
   g.bn = 256;

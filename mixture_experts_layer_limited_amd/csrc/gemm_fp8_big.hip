@@ -23,7 +23,9 @@
 // and B (weight rows) stream into LDS rings of 2 and 3 slots of 32 KB by
 // buffer_load ... lds; one "s_waitcnt vmcnt; s_barrier" per K step.  The
 // activation scales of a step (k-block-major over the permuted rows) go to
-// registers by buffer loads issued with the previous step's ring DMAs.
+// registers by buffer loads issued with the previous step's ring DMAs; a
+// tile's weight-block scales sit in one register per wave (lane = K step, so
+// K <= 64 * 128), read per step with readlane.
 #include "common.h"
 #include "kernels.h"
 #include "lds_dma.h"
@@ -146,7 +148,8 @@ __global__ __launch_bounds__(kBigNW * 64, 1) void gemm_fp8_big_kernel(GemmFp8Par
   for (int i = 0; i < TM; ++i)
     if ((wm + WM * i) * 16 < rows) tm_live = i + 1;
   tm_live = __builtin_amdgcn_readfirstlane(tm_live);
-  uint32_t vos[TM];  // scale offsets of the lane's token in each block
+  // scale offsets of the lane's token in each token block
+  uint32_t vos[TM];
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int r = (wm + WM * i) * 16 + lt;
@@ -166,6 +169,8 @@ __global__ __launch_bounds__(kBigNW * 64, 1) void gemm_fp8_big_kernel(GemmFp8Par
     srow_u = srow_g;
   }
   const uint32_t vsg = (uint32_t)(srow_g * nk * 4), vsu = (uint32_t)(srow_u * nk * 4);
+  // Lane l holds step l's weight-block scales (one load per tile, read per step
+  // with readlane): at most 64 K steps, which the launch checks.
 
   const int sw = swz<ROW>(lt);  // (row & 15) == lt for every 16-row block
   const int c0 = ((2 * lg) ^ sw) * 16, c1 = ((2 * lg + 1) ^ sw) * 16;
@@ -193,27 +198,37 @@ __global__ __launch_bounds__(kBigNW * 64, 1) void gemm_fp8_big_kernel(GemmFp8Par
     _Pragma("unroll") for (int i = (lo_); i < (hi_); ++i)                              \
       dma16(rb, dst_ + (wave * BI + i) * 1024, vob[i], soff_);                         \
   } while (0)
-// The scales of step kt_: the lane's activation scale in each token block and
-// the wave's weight-block scales (gate / up, or the one row).  Vector loads,
-// issued with the ring DMAs, so the step's barrier wait covers them.
+// The scales of step kt_: the lane's activation scale in each token block
+// (vector loads, issued with the ring DMAs, so the step's barrier wait covers
+// them) and the wave's weight-block scales (gate / up, or the one row), read
+// from the tile's scale registers.
 #define MOE_BIG_LOAD_SCALES(kt_)                                                       \
   do {                                                                                 \
     const uint32_t so_ = (kt_) < nk ? (uint32_t)(kt_) * sstep : 0x80000000u;           \
     _Pragma("unroll") for (int i = 0; i < TM; ++i) sa_n[i] = buffer_load_f32(rs, vos[i], so_); \
-    const uint32_t sw_ = (kt_) < nk ? (uint32_t)(kt_) * 4u : 0x80000000u;              \
-    sb_n[0] = buffer_load_f32(rws, vsg, sw_);                                          \
-    sb_n[1] = EPI == EPI_SWIGLU ? buffer_load_f32(rws, vsu, sw_) : sb_n[0];            \
+    const int l_ = min((kt_), 63); /* past the last step: a value never used */        \
+    sb_n[0] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wsg), l_)); \
+    sb_n[1] = EPI == EPI_SWIGLU                                                        \
+                  ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wsu), l_)) \
+                  : sb_n[0];                                                           \
   } while (0)
 
-  // Prologue, in the steady state's issue order: scales(0), A(0), B(0), then B(1).
+  // Prologue: the tile's weight-block scales (lane l: step l), then in the
+  // steady state's issue order scales(0), A(0), B(0) and B(1).
   // The scale products of the next step (activation scale x weight scale, per
   // token block: gate sg, up su) are carried from step to step; computing them
   // at the end of a step costs no wait the next barrier would not make anyway.
   float sa_n[TM], sb_n[2], sg_[TM], su_[TM];
+  float wsg, wsu = 0.0f;
+  wsg = buffer_load_f32(rws, lane < nk ? vsg + (uint32_t)lane * 4u : 0x80000000u, 0);
+  if constexpr (EPI == EPI_SWIGLU) wsu = buffer_load_f32(rws, lane < nk ? vsu + (uint32_t)lane * 4u : 0x80000000u, 0);
+  __builtin_amdgcn_sched_barrier(0);
   MOE_BIG_LOAD_SCALES(0);
+  __builtin_amdgcn_sched_barrier(0);
   MOE_BIG_ISSUE_A(0, 0);
   MOE_BIG_ISSUE_B(0, 0, 0, BI);
   MOE_BIG_ISSUE_B(1, 1, 0, BI);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     sg_[i] = sa_n[i] * sb_n[0];
@@ -403,6 +418,7 @@ static hipError_t launch_big(const GemmFp8Params& p, int grid_m, hipStream_t s) 
 
 hipError_t launch_gemm_fp8_big(int epi, const GemmFp8Params& p, int grid_m, hipStream_t s) {
   if (p.as_stride <= 0) return hipErrorInvalidValue;  // k-block-major activation scales only
+  if (p.K > kFp8BigMaxK) return hipErrorInvalidValue;  // one weight-scale register per wave
   switch (epi) {
     case EPI_SWIGLU:
       if (!p.Cq || !p.Cs) return hipErrorInvalidValue;

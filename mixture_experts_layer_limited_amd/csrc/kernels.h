@@ -96,7 +96,8 @@ struct GemmFp8Params {
   int64_t a_nrows;        // rows of A and of its scales (bounds of the activation buffers)
 };
 // rows_hint = mean rows per group; epi = the epilogue the launch will use
-GemmShape gemm_fp8_shape(int rows_hint, int epi);
+constexpr int kFp8BigMaxK = 64 * 128;
+GemmShape gemm_fp8_shape(int rows_hint, int epi, int K);
 hipError_t launch_gemm_fp8(int epi, const GemmFp8Params& p, const GemmShape& g, int grid_m, hipStream_t s);
 // 256 x 256 tiles (SwiGLU and row-store epilogues; k-block-major activation scales)
 hipError_t launch_gemm_fp8_big(int epi, const GemmFp8Params& p, int grid_m, hipStream_t s);
