@@ -267,6 +267,11 @@ SMALL = {
     # 256-row FP8 tiles, one group each (~250 rows: every token block of a tile live)
     "fp8_big_full_tiles": _reduced("v3_fp8", tokens=500, hidden=768, inter=256, n_experts=8, n_group=1,
                                    topk_group=1, top_k=4, shared_inter=256),
+    # FP8 with H past the 64 K steps whose weight-block scales the 256-row kernel keeps in
+    # one register: the gate/up GEMM takes the 128 x 256 kernel, the down GEMM (K = I) the
+    # 256 x 256 one, so the two GEMMs use tile lists of different heights
+    "fp8_wide_k": _reduced("v3_fp8", tokens=600, hidden=8320, inter=256, n_experts=8, n_group=1,
+                           topk_group=1, top_k=4, shared_inter=256),
     # 4-bit weights: shared expert merged as one more group (Is == I, T <= 1024)
     "w4_small": _reduced("v3_decode_w4a16", tokens=300, hidden=1024, inter=256, n_experts=64, shared_inter=256,
                          bias="zero"),
