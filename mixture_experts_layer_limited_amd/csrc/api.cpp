@@ -130,7 +130,9 @@ int router_splits(const moe_config* c, int64_t T) {
   if (sh.kind < 10) return 1;  // only the pipelined kernel splits K
   const int64_t tiles = ((T + sh.bm - 1) / sh.bm) * ((c->n_experts + sh.bn - 1) / sh.bn);
   const int nk = c->hidden / 64;
-  int want = (int)((512 + tiles - 1) / tiles);
+  // two rounds of 64-row tiles over the chip's CUs, or one of 128-row tiles
+  const int64_t groups = sh.bm >= 128 ? kChipCUs : 2 * kChipCUs;
+  int want = (int)((groups + tiles - 1) / tiles);
   if (want > 64) want = 64;
   int best = 1;
   for (int d = 1; d <= nk && d <= want; ++d)

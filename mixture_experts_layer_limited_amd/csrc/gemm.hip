@@ -281,7 +281,9 @@ static int tile_bn(int kind) { return kind == 0 ? 128 : 256; }
 GemmShape gemm_shape(int which, int dt, int rows_hint, int64_t tiles256) {
   int kind;
   if (dt != MOE_DT_BF16) kind = (which != 2 && rows_hint <= 32) ? 1 : 0;
-  else if (which == 2) kind = 14;  // router: 64 x 256 tiles, split K
+  // router, split K: 64 x 256 tiles, or 128 x 256 for large batches, where the
+  // gate weight re-read by every m-tile is most of the bytes
+  else if (which == 2) kind = rows_hint >= kRouterWideRows ? 12 : 14;
   else if (rows_hint <= 32) kind = which == 1 ? 13 : 14;
   else if (rows_hint < 128) kind = 12;
   // a launch with fewer 256 x 256 tiles than the chip has CUs leaves CUs idle

@@ -44,6 +44,8 @@ struct GemmShape {
 
 // MI355X: 256 compute units.
 constexpr int kChipCUs = 256;
+// Batches from this many tokens up take 128 x 256 router tiles.
+constexpr int kRouterWideRows = 4096;
 GemmShape gemm_shape(int which, int dt, int rows_hint, int64_t tiles256 = 0);
 hipError_t launch_gemm(int dt, int epi, int odt, const GemmParams& p, const GemmShape& g, int grid_m,
                        hipStream_t s);
