@@ -88,12 +88,16 @@ def test_route_selection_bit_exact(T, E, k, ng, tg, bias, ties):
     np.testing.assert_allclose(w.cpu().numpy(), wref, rtol=2e-6, atol=1e-7)
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "v2_lite_bf16", "v3_prefill_bf16", "v3_decode_bf16", "v3_fp8"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "v2_lite_bf16", "v3_prefill_bf16", "v3_decode_bf16", "v3_fp8",
+                                  "v3_prefill_bf16@4173", "v3_prefill_bf16@4095"])
 def test_route_from_hidden(name):
     """Router GEMM + scoring + selection on the workload's own x and gate
     weight (full T): scores against the fp64 oracle, selection bit-exact from
-    the GPU scores, and the fraction of tokens whose fp64 routing differs."""
-    cfg = PRESETS[name]
+    the GPU scores, and the fraction of tokens whose fp64 routing differs.
+    "name@T" runs the workload's layer on T tokens: 4173 gives the 128-row
+    router tiles a ragged last tile, 4095 is the last batch on 64-row tiles."""
+    base, _, t = name.partition("@")
+    cfg = PRESETS[base] if not t else PRESETS[base].replace(tokens=int(t))
     say(f"route from hidden {name} T={cfg.tokens}")
     from moe_inputs import routing_inputs
     r = routing_inputs(cfg, 0)
