@@ -226,6 +226,24 @@ bool merge_shared(const moe_config* c, int64_t T, bool scatter) {
          T <= kMergeSharedMaxT;
 }
 
+// The shared expert as a dense SwiGLU of its own: n_experts = 1, top-k 1.
+moe_config shared_config(const moe_config* c) {
+  moe_config sc = *c;
+  sc.n_experts = 1; sc.top_k = 1; sc.inter = c->shared_inter; sc.n_group = 1; sc.topk_group = 1;
+  return sc;
+}
+
+// FP8 weights, stored rows and the shared expert in dense launches of its own
+// on the 256 x 256 FP8 kernel: the shared down GEMM runs last and its epilogue
+// also does the layer's combine (the shared rows never reach HBM).  bf16 keeps
+// the combine kernel: there the fused epilogue's gathers ran no faster than the
+// combine kernel's, so it saved nothing measurable.
+bool fuse_combine(const moe_config* c, int64_t T, bool scatter) {
+  if (!is_fp8(c) || scatter || c->shared_inter <= 0 || merge_shared(c, T, scatter)) return false;
+  const moe_config sc = shared_config(c);
+  return tile_shape2(&sc, T, 1, c->shared_inter, false).kind == 2;
+}
+
 struct ForwardWs {
   RouteWs route;
   PermuteWs perm;
@@ -333,7 +351,8 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
               const float* hidden_scales, const int32_t* src, const int32_t* offsets, const void* w13,
               const float* w13_s, const void* w2, const float* w2_s, int epi, const float* topk_w,
               const int32_t* inv, void* out, float* acc, const SwigluWs& w, hipStream_t s,
-              hipEvent_t const* ev = nullptr, const SharedGroup* sg = nullptr, bool tiles_ready = false) {
+              hipEvent_t const* ev = nullptr, const SharedGroup* sg = nullptr, bool tiles_ready = false,
+              const CombineEpi* cb = nullptr) {
   auto mark = [&](int i) -> int {
     if (ev && ev[i]) return hip_status(hipEventRecord(ev[i], s));
     return MOE_OK;
@@ -388,6 +407,7 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
       HIP_TRY(launch_gemm_fp8(EPI_SCATTER, q, g2, gm2, s));
     } else {
       q.C = out;
+      if (cb) q.comb = *cb;
       MOE_TRY(mark(2));
       HIP_TRY(launch_gemm_fp8(EPI_STORE, q, g2, gm2, s));
     }
@@ -680,9 +700,9 @@ int moe_forward(const moe_config* c, int64_t T, const void* hidden, const void* 
     xin = w.routed.xq;
     xs = w.routed.xs;
   }
-  if (c->shared_inter > 0 && !merged) {
-    moe_config sc = *c;
-    sc.n_experts = 1; sc.top_k = 1; sc.inter = c->shared_inter; sc.n_group = 1; sc.topk_group = 1;
+  const bool fused = fuse_combine(c, T, scatter);
+  const moe_config sc = shared_config(c);
+  if (c->shared_inter > 0 && !merged && !fused) {
     MOE_TRY(do_swiglu(&sc, T, T, 1, c->shared_inter, xin, xs, nullptr, nullptr, sh_w13, sh_w13_scales, sh_w2,
                       sh_w2_scales, MOE_EPI_STORE_ROWS, nullptr, nullptr, w.sh_out, nullptr, w.shared, stream));
   }
@@ -691,6 +711,15 @@ int moe_forward(const moe_config* c, int64_t T, const void* hidden, const void* 
   MOE_TRY(do_swiglu(c, T, rows_all, groups, c->inter, xin, xs, src, offsets, w13, w13_scales, w2, w2_scales, epi,
                     topw, inv, w.y, w.acc, w.routed, stream, opts ? opts->events : nullptr, merged ? &sg : nullptr,
                     tiles_ready));
+  if (fused) {
+    // the shared expert last: its down GEMM's epilogue combines the routed rows
+    // with its own and writes the layer output
+    CombineEpi cb;
+    cb.rows = w.y; cb.inv = inv; cb.w = topw; cb.k = c->top_k; cb.out = out;
+    return do_swiglu(&sc, T, T, 1, c->shared_inter, xin, xs, nullptr, nullptr, sh_w13, sh_w13_scales, sh_w2,
+                     sh_w2_scales, MOE_EPI_STORE_ROWS, nullptr, nullptr, w.sh_out, nullptr, w.shared, stream, nullptr,
+                     nullptr, false, &cb);
+  }
   const void* shared_rows = merged ? (const void*)((const char*)w.y + rows * c->hidden * act_bytes(c)) : w.sh_out;
   HIP_TRY(launch_combine(act_dt(c), (int)T, c->hidden, c->top_k, w.y, w.acc, inv, topw, shared_rows, out, stream));
   return MOE_OK;

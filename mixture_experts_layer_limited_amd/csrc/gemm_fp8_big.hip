@@ -26,6 +26,7 @@
 // registers by buffer loads issued with the previous step's ring DMAs; a
 // tile's weight-block scales sit in one register per wave (lane = K step, so
 // K <= 64 * 128), read per step with readlane.
+#include "combine_epi.h"
 #include "common.h"
 #include "kernels.h"
 #include "lds_dma.h"
@@ -394,6 +395,11 @@ __global__ __launch_bounds__(kBigNW * 64, 1) void gemm_fp8_big_kernel(GemmFp8Par
     __syncthreads();
     constexpr int CPRo = BN / 8;
     const int cbase = nt * BN;
+    if (p.comb.rows) {  // dense launch over tokens: the layer's combine instead of the row store
+      combine_staged_tile<BM, CPRo, RB, NW * 64, 4>(p.comb, lds, SA * ASLOT + SB * BSLOT - BM * RB, r0, rows, cbase,
+                                                 p.N, tid);
+      return;
+    }
     for (int q = tid; q < BM * CPRo; q += NW * 64) {
       const int row = q / CPRo, ch = q % CPRo;
       const int col = cbase + ch * 8;

@@ -12,6 +12,19 @@ namespace moe {
 enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1, MOE_DT_FP8 = 2 };
 enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SCATTER = 2 };
 
+// Dense row-store launch over the T tokens (the shared expert's down GEMM on
+// the 256 x 256 FP8 kernel) whose epilogue also does the layer's weighted
+// un-permute + combine: with rows != NULL it writes
+// out[t] = sum_j w[t*k+j] * rows[inv[t*k+j]] + C-tile[t] (bf16) instead of
+// storing its own rows.
+struct CombineEpi {
+  const void* rows = nullptr;   // routed expert rows in permuted order, [T*k, N] bf16
+  const int32_t* inv = nullptr; // inv_perm [T*k]
+  const float* w = nullptr;     // routing weights [T*k]
+  int k = 0;
+  void* out = nullptr;          // [T, N] bf16
+};
+
 struct GemmParams {
   const void* A;          // activations: row src(p) at A + src(p) * K elements
   const int32_t* a_rows;  // src(p) = a_rows[p]; NULL: src(p) = p
@@ -96,6 +109,7 @@ struct GemmFp8Params {
   int M;
   int ntn;
   int64_t a_nrows;        // rows of A and of its scales (bounds of the activation buffers)
+  CombineEpi comb;        // 256 x 256 kernel, dense row store only
 };
 // rows_hint = mean rows per group; epi = the epilogue the launch will use
 constexpr int kFp8BigMaxK = 64 * 128;

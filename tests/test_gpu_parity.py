@@ -276,6 +276,10 @@ SMALL = {
     # 256 x 256 one, so the two GEMMs use tile lists of different heights
     "fp8_wide_k": _reduced("v3_fp8", tokens=600, hidden=8320, inter=256, n_experts=8, n_group=1,
                            topk_group=1, top_k=4, shared_inter=256),
+    # bf16 shared expert in dense launches of 256 x 256 tiles (at least one per CU);
+    # ragged last m-tile and n-tile
+    "dense_shared_256": _reduced("v3_prefill_bf16", tokens=2100, hidden=8256, inter=128, n_experts=16, n_group=4,
+                              topk_group=2, top_k=2, shared_inter=128),
     # 4-bit weights: shared expert merged as one more group (Is == I, T <= 1024)
     "w4_small": _reduced("v3_decode_w4a16", tokens=300, hidden=1024, inter=256, n_experts=64, shared_inter=256,
                          bias="zero"),
@@ -455,13 +459,20 @@ def test_shared_expert_through_grouped_call():
     assert rel_err(f64(rows), ref) <= TOL["bf16"]
 
 
-def test_staged_calls_match_forward():
+@pytest.mark.parametrize("name", ["v3_small", "dense_shared_256", "fp8_big", "fp8_big_ragged"])
+def test_staged_calls_match_forward(name):
     """route -> permute -> grouped_swiglu (routed and shared) -> combine gives
-    the same layer output as moe_forward, and both match the oracle."""
-    cfg = SMALL["v3_small"]
+    the same layer output as moe_forward, bit for bit, and both match the
+    oracle.  Inside moe_forward, v3_small runs the shared expert as one more
+    routed group and dense_shared_256 in dense bf16 launches of 256 x 256
+    tiles; in fp8_big and fp8_big_ragged (ragged n-tile) the shared down GEMM
+    on the 256 x 256 FP8 kernel also does the combine in its epilogue, which
+    the staged combine kernel checks bit for bit."""
+    cfg = SMALL[name]
     inp = layer_inputs(cfg, 3, DEV)
     c = binding_config(cfg)
     T, E, k, H, Is = cfg.tokens, cfg.n_experts, cfg.top_k, cfg.hidden, cfg.shared_inter
+    say(f"staged calls vs forward {name} T={T} H={H} Is={Is}")
     scores, ids, w = f32((T, E)), i32((T, k)), f32((T, k))
     # with a workspace, as moe_forward has one: the same split-K router GEMM
     moe.route(c, T, inp["x"], inp["gate_w"], inp["bias"], None, scores, ids, w,
@@ -470,22 +481,23 @@ def test_staged_calls_match_forward():
     moe.permute(c, T, ids, off, src, inv, moe.workspace(c, T, moe.MOE_OP_PERMUTE))
     rows = torch.empty(T * k, H, dtype=torch.bfloat16, device=DEV)
     ws = moe.workspace(c, T, moe.MOE_OP_GROUPED_SWIGLU)
-    moe.grouped_swiglu(c, T, inp["x"], None, src, off, inp["w13"], None, inp["w2"], None,
+    moe.grouped_swiglu(c, T, inp["x"], None, src, off, inp["w13"], inp["w13_s"], inp["w2"], inp["w2_s"],
                        moe.MOE_EPI_STORE_ROWS, None, None, rows, None, ws)
-    sc = moe.make_config(hidden=H, inter=Is, n_experts=1, top_k=1, dtype="bf16")
+    sc = moe.make_config(hidden=H, inter=Is, n_experts=1, top_k=1, dtype=cfg.dtype)
     sh = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
+    scale = lambda t: None if t is None else t[None]
     moe.grouped_swiglu(sc, T, inp["x"], None, None, torch.tensor([0, T], dtype=torch.int32, device=DEV),
-                       inp["sh_w13"][None], None, inp["sh_w2"][None], None, moe.MOE_EPI_STORE_ROWS, None, None,
-                       sh, None, ws)
+                       inp["sh_w13"][None], scale(inp["sh_w13_s"]), inp["sh_w2"][None], scale(inp["sh_w2_s"]),
+                       moe.MOE_EPI_STORE_ROWS, None, None, sh, None, moe.workspace(sc, T, moe.MOE_OP_GROUPED_SWIGLU))
     out = torch.empty(T, H, dtype=torch.bfloat16, device=DEV)
     moe.combine(c, T, rows, None, inv, w, sh, out)
     out2 = torch.empty_like(out)
-    moe.forward(c, T, inp["x"], inp["gate_w"], inp["bias"], inp["w13"], None, inp["w2"], None, inp["sh_w13"],
-                None, inp["sh_w2"], None, out2, moe.workspace(c, T))
+    moe.forward(c, T, inp["x"], inp["gate_w"], inp["bias"], inp["w13"], inp["w13_s"], inp["w2"], inp["w2_s"],
+                inp["sh_w13"], inp["sh_w13_s"], inp["sh_w2"], inp["sh_w2_s"], out2, moe.workspace(c, T))
     torch.cuda.synchronize()
-    assert torch.equal(out, out2)
+    assert torch.equal(out, out2), f"{(out != out2).sum().item()} elements differ"
     ids_r, w_r = oracle_routing(cfg, scores.cpu().numpy(), inp["bias"])
-    assert rel_err(f64(out), _oracle_full(cfg, inp, ids_r, w_r)) <= TOL["bf16"]
+    assert rel_err(f64(out), _oracle_full(cfg, inp, ids_r, w_r)) <= TOL[cfg.dtype]
 
 
 # ------------------------------------------------------ full-size workloads ---
