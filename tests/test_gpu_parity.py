@@ -265,6 +265,10 @@ SMALL = {
     # shared expert of the routed width in its own dense launches (T > 1024)
     "fp8_big": _reduced("v3_fp8", tokens=1100, hidden=512, inter=256, n_experts=16, n_group=4, topk_group=2,
                         top_k=4, shared_inter=256),
+    # FP8 with k = 16: the shared down GEMM's combine epilogue reads the routed rows'
+    # indices and weights from memory (16 per token do not fit its spare LDS)
+    "fp8_big_top_k16": _reduced("v3_fp8", tokens=1100, hidden=512, inter=256, n_experts=32, n_group=1,
+                                topk_group=1, top_k=16, shared_inter=256),
     # 256-row FP8 tiles with H a ragged number of 256-column n-tiles and I of 128-column ones
     "fp8_big_ragged": _reduced("v3_fp8", tokens=777, hidden=640, inter=384, n_experts=8, n_group=1, topk_group=1,
                                top_k=3, shared_inter=128),
@@ -459,15 +463,15 @@ def test_shared_expert_through_grouped_call():
     assert rel_err(f64(rows), ref) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("name", ["v3_small", "dense_shared_256", "fp8_big", "fp8_big_ragged"])
+@pytest.mark.parametrize("name", ["v3_small", "dense_shared_256", "fp8_big", "fp8_big_ragged", "fp8_big_top_k16"])
 def test_staged_calls_match_forward(name):
     """route -> permute -> grouped_swiglu (routed and shared) -> combine gives
     the same layer output as moe_forward, bit for bit, and both match the
     oracle.  Inside moe_forward, v3_small runs the shared expert as one more
     routed group and dense_shared_256 in dense bf16 launches of 256 x 256
-    tiles; in fp8_big and fp8_big_ragged (ragged n-tile) the shared down GEMM
-    on the 256 x 256 FP8 kernel also does the combine in its epilogue, which
-    the staged combine kernel checks bit for bit."""
+    tiles; in fp8_big, fp8_big_ragged (ragged n-tile) and fp8_big_top_k16 the
+    shared down GEMM on the 256 x 256 FP8 kernel also does the combine in its
+    epilogue, which the staged combine kernel checks bit for bit."""
     cfg = SMALL[name]
     inp = layer_inputs(cfg, 3, DEV)
     c = binding_config(cfg)
