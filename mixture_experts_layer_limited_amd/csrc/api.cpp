@@ -233,15 +233,16 @@ moe_config shared_config(const moe_config* c) {
   return sc;
 }
 
-// FP8 weights, stored rows and the shared expert in dense launches of its own
-// on the 256 x 256 FP8 kernel: the shared down GEMM runs last and its epilogue
-// also does the layer's combine (the shared rows never reach HBM).  bf16 keeps
-// the combine kernel: there the fused epilogue's gathers ran no faster than the
-// combine kernel's, so it saved nothing measurable.
+// Stored rows and the shared expert in dense launches of its own on a 256 x 256
+// kernel (bf16 or FP8): the shared down GEMM runs last and its EPI_COMBINE
+// epilogue also does the layer's combine, so the shared rows never reach HBM
+// and the combine kernel is not launched.
 bool fuse_combine(const moe_config* c, int64_t T, bool scatter) {
-  if (!is_fp8(c) || scatter || c->shared_inter <= 0 || merge_shared(c, T, scatter)) return false;
+  if (scatter || c->shared_inter <= 0 || merge_shared(c, T, scatter)) return false;
+  if (act_dt(c) != MOE_DT_BF16 || is_w4(c)) return false;
   const moe_config sc = shared_config(c);
-  return tile_shape2(&sc, T, 1, c->shared_inter, false).kind == 2;
+  const GemmShape g = tile_shape2(&sc, T, 1, c->shared_inter, false);
+  return is_fp8(c) ? g.kind == 2 : g.kind == 15;
 }
 
 struct ForwardWs {
@@ -409,7 +410,7 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
       q.C = out;
       if (cb) q.comb = *cb;
       MOE_TRY(mark(2));
-      HIP_TRY(launch_gemm_fp8(EPI_STORE, q, g2, gm2, s));
+      HIP_TRY(launch_gemm_fp8(cb ? EPI_COMBINE : EPI_STORE, q, g2, gm2, s));
     }
     return mark(3);
   }
@@ -492,8 +493,9 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
     HIP_TRY(launch_gemm(dt, EPI_SCATTER, MOE_DT_F32, q, g2, gm2, s));
   } else {
     q.C = out;
+    if (cb) q.comb = *cb;
     MOE_TRY(mark(2));
-    HIP_TRY(launch_gemm(dt, EPI_STORE, dt, q, g2, gm2, s));
+    HIP_TRY(launch_gemm(dt, cb ? EPI_COMBINE : EPI_STORE, dt, q, g2, gm2, s));
   }
   return mark(3);
 }

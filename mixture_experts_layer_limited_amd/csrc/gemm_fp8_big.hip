@@ -59,7 +59,8 @@ constexpr int kBigLds = (kBigSA * kBigBM + kBigSB * kBigBN) * 128;
 
 template <int EPI>
 __global__ __launch_bounds__(kBigNW * 64, 1) void gemm_fp8_big_kernel(GemmFp8Params p) {
-  static_assert(EPI == EPI_SWIGLU || EPI == EPI_STORE, "transposed blocks: SwiGLU and row-store epilogues");
+  static_assert(EPI == EPI_SWIGLU || EPI == EPI_STORE || EPI == EPI_COMBINE,
+                "transposed blocks: SwiGLU and row-store epilogues");
   constexpr int WM = kBigWM, WN = kBigWN, NW = kBigNW;
   constexpr int BM = kBigBM, BN = kBigBN, TM = kBigTM, TN = kBigTN;
   constexpr int SA = kBigSA, SB = kBigSB;
@@ -395,7 +396,7 @@ __global__ __launch_bounds__(kBigNW * 64, 1) void gemm_fp8_big_kernel(GemmFp8Par
     __syncthreads();
     constexpr int CPRo = BN / 8;
     const int cbase = nt * BN;
-    if (p.comb.rows) {  // dense launch over tokens: the layer's combine instead of the row store
+    if constexpr (EPI == EPI_COMBINE) {  // dense launch over tokens: the layer's combine instead of the row store
       combine_staged_tile<BM, CPRo, RB, NW * 64, 4>(p.comb, lds, SA * ASLOT + SB * BSLOT - BM * RB, r0, rows, cbase,
                                                  p.N, tid);
       return;
@@ -430,6 +431,9 @@ hipError_t launch_gemm_fp8_big(int epi, const GemmFp8Params& p, int grid_m, hipS
       if (!p.Cq || !p.Cs) return hipErrorInvalidValue;
       return launch_big<EPI_SWIGLU>(p, grid_m, s);
     case EPI_STORE: return launch_big<EPI_STORE>(p, grid_m, s);
+    case EPI_COMBINE:
+      if (!p.comb.rows || !p.comb.inv || !p.comb.w || !p.comb.out || p.comb.k <= 0 || p.tiles) return hipErrorInvalidValue;
+      return launch_big<EPI_COMBINE>(p, grid_m, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -24,6 +24,7 @@
 // balanced when a tile has fewer live rows than BM; row blocks without live rows
 // issue no MFMAs (the live blocks of a wave are a prefix, so the K loop is
 // specialised on their count and stays branch-free).
+#include "combine_epi.h"
 #include "common.h"
 #include "kernels.h"
 #include "lds_dma.h"
@@ -442,7 +443,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_split_kernel(GemmParams 
 #undef MOE_SPLIT_ISSUE_A
 #undef MOE_SPLIT_ISSUE_B
 
-  if constexpr (ODT == MOE_DT_BF16 && (EPI == EPI_STORE || EPI == EPI_SWIGLU)) {
+  if constexpr (ODT == MOE_DT_BF16 && (EPI == EPI_STORE || EPI == EPI_SWIGLU || EPI == EPI_COMBINE)) {
     // bf16 tile through LDS (the ring is idle now), then 16-byte row-contiguous
     // global stores.  Lanes l and l^1 trade one value per row pair (DPP) so each
     // lane writes two adjacent columns of one row as a dword: even lanes row r,
@@ -480,6 +481,11 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_split_kernel(GemmParams 
     __syncthreads();
     constexpr int CPRo = OC / 8;  // 16-byte chunks per output row
     const int c0 = nt * OC;
+    if constexpr (EPI == EPI_COMBINE) {  // dense launch over tokens: the layer's combine instead of the row store
+      combine_staged_tile<BM, CPRo, RB, NW * 64, 4>(p.comb, lds, SA * ASLOT + SB * BSLOT - BM * RB, r0, rows, c0,
+                                                   p.N, tid);
+      return;
+    }
     for (int q = tid; q < BM * CPRo; q += NW * 64) {
       const int row = q / CPRo, ch = q % CPRo;
       const int col = c0 + ch * 8;
@@ -578,6 +584,11 @@ hipError_t launch_gemm_pipe(int epi, int odt, const GemmParams& p, const GemmSha
   switch (epi) {
     case EPI_SWIGLU: return pipe_kind<EPI_SWIGLU, MOE_DT_BF16>(p, g, grid_m, s);
     case EPI_SCATTER: return pipe_kind<EPI_SCATTER, MOE_DT_F32>(p, g, grid_m, s);
+    case EPI_COMBINE:  // the 256 x 256 split-ring kernel only, dense, bf16 out
+      if (g.kind != 15 || odt != MOE_DT_BF16 || p.tiles || !p.comb.rows || !p.comb.inv || !p.comb.w || !p.comb.out ||
+          p.comb.k <= 0)
+        return hipErrorInvalidValue;
+      return launch_split<2, 2, 4, 4, 2, 3, EPI_COMBINE, MOE_DT_BF16>(p, grid_m, s);
     default:
       if (odt == MOE_DT_F32) return pipe_kind<EPI_STORE, MOE_DT_F32>(p, g, grid_m, s);
       return pipe_kind<EPI_STORE, MOE_DT_BF16>(p, g, grid_m, s);

@@ -10,13 +10,14 @@
 namespace moe {
 
 enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1, MOE_DT_FP8 = 2 };
-enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SCATTER = 2 };
+// EPI_COMBINE: a row store over the T tokens of a dense launch (the shared
+// expert's down GEMM) whose tile is combined with the routed rows (CombineEpi)
+// and written as the layer output; 256 x 256 bf16 and FP8 kernels only.
+enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_SCATTER = 2, EPI_COMBINE = 3 };
 
-// Dense row-store launch over the T tokens (the shared expert's down GEMM on
-// the 256 x 256 FP8 kernel) whose epilogue also does the layer's weighted
-// un-permute + combine: with rows != NULL it writes
-// out[t] = sum_j w[t*k+j] * rows[inv[t*k+j]] + C-tile[t] (bf16) instead of
-// storing its own rows.
+// The EPI_COMBINE epilogue's inputs: it writes
+// out[t] = sum_j w[t*k+j] * rows[inv[t*k+j]] + C-tile[t] (bf16), the layer's
+// weighted un-permute + combine, instead of storing the launch's own rows.
 struct CombineEpi {
   const void* rows = nullptr;   // routed expert rows in permuted order, [T*k, N] bf16
   const int32_t* inv = nullptr; // inv_perm [T*k]
@@ -47,6 +48,7 @@ struct GemmParams {
   // slices of K / ksplit columns each; slice z writes C + z * c_split_stride.
   int ksplit;             // 0 or 1: no split
   int64_t c_split_stride; // elements between the slices' outputs
+  CombineEpi comb;        // EPI_COMBINE
 };
 
 struct GemmShape {
@@ -109,7 +111,7 @@ struct GemmFp8Params {
   int M;
   int ntn;
   int64_t a_nrows;        // rows of A and of its scales (bounds of the activation buffers)
-  CombineEpi comb;        // 256 x 256 kernel, dense row store only
+  CombineEpi comb;        // EPI_COMBINE
 };
 // rows_hint = mean rows per group; epi = the epilogue the launch will use
 constexpr int kFp8BigMaxK = 64 * 128;

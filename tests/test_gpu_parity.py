@@ -280,8 +280,8 @@ SMALL = {
     # 256 x 256 one, so the two GEMMs use tile lists of different heights
     "fp8_wide_k": _reduced("v3_fp8", tokens=600, hidden=8320, inter=256, n_experts=8, n_group=1,
                            topk_group=1, top_k=4, shared_inter=256),
-    # bf16 shared expert in dense launches of 256 x 256 tiles (at least one per CU);
-    # ragged last m-tile and n-tile
+    # bf16 shared expert in dense launches of 256 x 256 tiles (at least one per CU), whose
+    # down GEMM's epilogue also does the layer's combine; ragged last m-tile and n-tile
     "dense_shared_256": _reduced("v3_prefill_bf16", tokens=2100, hidden=8256, inter=128, n_experts=16, n_group=4,
                               topk_group=2, top_k=2, shared_inter=128),
     # 4-bit weights: shared expert merged as one more group (Is == I, T <= 1024)
@@ -468,10 +468,10 @@ def test_staged_calls_match_forward(name):
     """route -> permute -> grouped_swiglu (routed and shared) -> combine gives
     the same layer output as moe_forward, bit for bit, and both match the
     oracle.  Inside moe_forward, v3_small runs the shared expert as one more
-    routed group and dense_shared_256 in dense bf16 launches of 256 x 256
-    tiles; in fp8_big, fp8_big_ragged (ragged n-tile) and fp8_big_top_k16 the
-    shared down GEMM on the 256 x 256 FP8 kernel also does the combine in its
-    epilogue, which the staged combine kernel checks bit for bit."""
+    routed group; in the others its down GEMM runs on a 256 x 256 kernel whose
+    epilogue also does the combine (dense_shared_256: bf16; fp8_big,
+    fp8_big_ragged with a ragged n-tile, fp8_big_top_k16 with k = 16: FP8),
+    which the staged combine kernel checks bit for bit."""
     cfg = SMALL[name]
     inp = layer_inputs(cfg, 3, DEV)
     c = binding_config(cfg)
