@@ -268,6 +268,10 @@ int moe_combine(const moe_config* cfg, int64_t T, const void* expert_out, const 
  *   when Is == 0;
  *   out [T,H] act_dtype; opts may be NULL (store-rows epilogue, no extra
  *   outputs).
+ * The result equals that of the staged calls bit for bit.  Where the shared
+ * expert runs as dense launches of 256 x 256 tiles with stored rows, its down
+ * GEMM runs last and does the combine in its epilogue (same sums, same order),
+ * so no combine launch and no shared-expert rows in memory.
  */
 int moe_forward(const moe_config* cfg, int64_t T, const void* hidden, const void* gate_w,
                 const float* bias, const void* w13, const float* w13_scales, const void* w2,
