@@ -15,10 +15,11 @@
 namespace moe {
 
 // The gather-combine of chunks q = tid, tid + NT, ... (see combine_staged_tile),
-// G chunks at a time (G * 8 row gathers of 16 bytes in flight per thread): every chunk's routed-row indices and weights first (from
-// LDS when STAGED, else from memory), then all its row gathers, then the sums.
-// Lanes without an entry gather a valid row (0) and keep their sum by select,
-// so the loads are issued unconditionally and stay in flight together.
+// G chunks at a time, up to G * 8 row gathers of 16 bytes in flight per thread:
+// every chunk's routed-row indices and weights first (from LDS when STAGED,
+// else from memory), then all its row gathers, then the sums.  Lanes without
+// an entry gather a valid row (0) and keep their sum by select, so the loads
+// are issued unconditionally and stay in flight together.
 template <bool STAGED, int BM, int CPR, int RB, int NT, int G>
 __device__ __forceinline__ void combine_chunks(const CombineEpi& cb, const char* lds, const int* pos_l,
                                                const float* w_l, int64_t base, int r0, int rows, int c0, int N,

@@ -432,7 +432,8 @@ hipError_t launch_gemm_fp8_big(int epi, const GemmFp8Params& p, int grid_m, hipS
       return launch_big<EPI_SWIGLU>(p, grid_m, s);
     case EPI_STORE: return launch_big<EPI_STORE>(p, grid_m, s);
     case EPI_COMBINE:
-      if (!p.comb.rows || !p.comb.inv || !p.comb.w || !p.comb.out || p.comb.k <= 0 || p.tiles) return hipErrorInvalidValue;
+      if (!p.comb.rows || !p.comb.inv || !p.comb.w || !p.comb.out || p.comb.k <= 0 || p.tiles)
+        return hipErrorInvalidValue;  // dense launches over tokens only
       return launch_big<EPI_COMBINE>(p, grid_m, s);
     default: return hipErrorInvalidValue;
   }
