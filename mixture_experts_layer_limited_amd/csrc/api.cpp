@@ -347,13 +347,14 @@ struct SharedGroup {
 };
 
 // One grouped SwiGLU: routed experts (offsets given) or a dense FFN over all
-// rows (offsets == nullptr, the shared expert).
+// rows (offsets == nullptr, the shared expert).  phase 1 launches only the
+// gate/up GEMM, phase 2 only the down GEMM (0: both).
 int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, const void* hidden,
               const float* hidden_scales, const int32_t* src, const int32_t* offsets, const void* w13,
               const float* w13_s, const void* w2, const float* w2_s, int epi, const float* topk_w,
               const int32_t* inv, void* out, float* acc, const SwigluWs& w, hipStream_t s,
               hipEvent_t const* ev = nullptr, const SharedGroup* sg = nullptr, bool tiles_ready = false,
-              const CombineEpi* cb = nullptr) {
+              const CombineEpi* cb = nullptr, int phase = 0) {
   auto mark = [&](int i) -> int {
     if (ev && ev[i]) return hip_status(hipEventRecord(ev[i], s));
     return MOE_OK;
@@ -376,7 +377,7 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
     }
     GemmFp8Params p{};
     // the kernel reads the activation scales k-block-major over the permuted rows
-    HIP_TRY(launch_gather_scales_t(xs, src, rows, H / 128, T, w.xs_t, s));
+    if (phase != 2) HIP_TRY(launch_gather_scales_t(xs, src, rows, H / 128, T, w.xs_t, s));
     p.A = xq; p.a_scales = w.xs_t; p.as_stride = rows; p.a_rows = src;
     p.B = (const uint8_t*)w13; p.b_scales = w13_s;
     p.b_gstride = (int64_t)2 * I * H; p.bs_gstride = (int64_t)(2 * I / 128) * (H / 128);
@@ -389,7 +390,7 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
     p.ntn = ntn1;
     const int gm1 = dense ? p.n_mtiles : max_mtiles(rows, g1.bm, groups);
     MOE_TRY(mark(0));
-    HIP_TRY(launch_gemm_fp8(EPI_SWIGLU, p, g1, gm1, s));
+    if (phase != 2) HIP_TRY(launch_gemm_fp8(EPI_SWIGLU, p, g1, gm1, s));
     MOE_TRY(mark(1));
     GemmFp8Params q{};
     q.A = w.hq; q.a_scales = w.h_scales; q.a_rows = nullptr; q.as_stride = rows;
@@ -410,7 +411,7 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
       q.C = out;
       if (cb) q.comb = *cb;
       MOE_TRY(mark(2));
-      HIP_TRY(launch_gemm_fp8(cb ? EPI_COMBINE : EPI_STORE, q, g2, gm2, s));
+      if (phase != 1) HIP_TRY(launch_gemm_fp8(cb ? EPI_COMBINE : EPI_STORE, q, g2, gm2, s));
     }
     return mark(3);
   }
@@ -474,7 +475,8 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
   set_tiles(p, dense, rows, g1.bm, w.tiles1, w.ntiles1);
   p.ntn = ntn1;
   MOE_TRY(mark(0));
-  HIP_TRY(launch_gemm(dt, EPI_SWIGLU, dt, p, g1, dense ? p.n_mtiles : max_mtiles(rows, g1.bm, groups), s));
+  if (phase != 2)
+    HIP_TRY(launch_gemm(dt, EPI_SWIGLU, dt, p, g1, dense ? p.n_mtiles : max_mtiles(rows, g1.bm, groups), s));
   MOE_TRY(mark(1));
 
   GemmParams q{};
@@ -495,7 +497,7 @@ int do_swiglu(const moe_config* c, int64_t T, int64_t rows, int groups, int I, c
     q.C = out;
     if (cb) q.comb = *cb;
     MOE_TRY(mark(2));
-    HIP_TRY(launch_gemm(dt, cb ? EPI_COMBINE : EPI_STORE, dt, q, g2, gm2, s));
+    if (phase != 1) HIP_TRY(launch_gemm(dt, cb ? EPI_COMBINE : EPI_STORE, dt, q, g2, gm2, s));
   }
   return mark(3);
 }
@@ -704,9 +706,10 @@ int moe_forward(const moe_config* c, int64_t T, const void* hidden, const void* 
   }
   const bool fused = fuse_combine(c, T, scatter);
   const moe_config sc = shared_config(c);
-  if (c->shared_inter > 0 && !merged && !fused) {
+  if (c->shared_inter > 0 && !merged) {
     MOE_TRY(do_swiglu(&sc, T, T, 1, c->shared_inter, xin, xs, nullptr, nullptr, sh_w13, sh_w13_scales, sh_w2,
-                      sh_w2_scales, MOE_EPI_STORE_ROWS, nullptr, nullptr, w.sh_out, nullptr, w.shared, stream));
+                      sh_w2_scales, MOE_EPI_STORE_ROWS, nullptr, nullptr, w.sh_out, nullptr, w.shared, stream,
+                      nullptr, nullptr, false, nullptr, fused ? 1 : 0));
   }
   if (scatter) HIP_TRY(launch_fill_zero(w.acc, T * c->hidden, stream));
   const SharedGroup sg{sh_w13, sh_w13_scales, sh_w2, sh_w2_scales, E};
@@ -714,13 +717,14 @@ int moe_forward(const moe_config* c, int64_t T, const void* hidden, const void* 
                     topw, inv, w.y, w.acc, w.routed, stream, opts ? opts->events : nullptr, merged ? &sg : nullptr,
                     tiles_ready));
   if (fused) {
-    // the shared expert last: its down GEMM's epilogue combines the routed rows
-    // with its own and writes the layer output
+    // the shared down GEMM last: its epilogue combines the routed rows with its
+    // own and writes the layer output (its gate/up GEMM ran before the routed
+    // GEMMs, which measured slightly faster than running it here)
     CombineEpi cb;
     cb.rows = w.y; cb.inv = inv; cb.w = topw; cb.k = c->top_k; cb.out = out;
     return do_swiglu(&sc, T, T, 1, c->shared_inter, xin, xs, nullptr, nullptr, sh_w13, sh_w13_scales, sh_w2,
                      sh_w2_scales, MOE_EPI_STORE_ROWS, nullptr, nullptr, w.sh_out, nullptr, w.shared, stream, nullptr,
-                     nullptr, false, &cb);
+                     nullptr, false, &cb, 2);
   }
   const void* shared_rows = merged ? (const void*)((const char*)w.y + rows * c->hidden * act_bytes(c)) : w.sh_out;
   HIP_TRY(launch_combine(act_dt(c), (int)T, c->hidden, c->top_k, w.y, w.acc, inv, topw, shared_rows, out, stream));
